@@ -1,0 +1,159 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer step.
+ *
+ * One call performs, for every 2-D weight in a list, the Muon step the speedrun
+ * pages describe:
+ *
+ *   m'  = beta * m + g                      momentum, no dampening
+ *   u   = g + beta * m'  (Nesterov)  or  m'
+ *   X0  = u / (||u||_F + eps),  transposed when rows > cols
+ *   ns_steps x { A = X X^T ; B = b A + c A A ; X = a X + B X }
+ *   O   = X (transposed back)
+ *   W'  = W * (1 - lr * wd) - lr * sqrt(max(1, rows/cols)) * O
+ *
+ * Sources: "14 -- modded-nanogpt: the Speedrun Community", section 3 "Muon"
+ * (pseudocode: momentum form, update sign, 5 iterations); "NanoGPT Speedrun"
+ * (modded-nanogpt README mirror), Muon section (the Newton-Schulz routine:
+ * eps = 1e-7 on the Frobenius norm, the transpose rule, coefficients
+ * (3.4445, -4.7750, 2.0315); the practices list: Nesterov momentum, bfloat16
+ * execution); same README, GPT-2 medium track ("standard weight decay").
+ * Readings where the pages are silent: the Nesterov form u = g + beta m', the
+ * decoupled lr-coupled decay on the old W, and the shape scale.
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major: element (i, j) at ptr[i * ld + j]; ld counts
+ *     elements and must be >= cols.
+ *   - Every data pointer is a device pointer on the handle's device, owned by
+ *     the caller, and must stay valid until the stream has passed the work.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without synchronising.  A handle owns one workspace:
+ *     calls on one handle must be ordered on one stream (or externally).
+ *   - Validation happens before anything is enqueued; a call that returns an
+ *     error enqueued nothing and changed no caller memory.
+ *   - NaN/Inf inputs are not checked; they propagate within their matrix.
+ *   - A handle is bound to one device and is not thread-safe; distinct handles
+ *     are independent.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARG = 1,  /* null pointer, bad size/ld, aliasing, bad ns_steps */
+    MUON_ERR_DTYPE = 2,        /* unknown storage dtype or compute mode */
+    MUON_ERR_NO_DEVICE = 3,    /* no HIP device, or the handle's device is gone */
+    MUON_ERR_OOM = 4,          /* workspace allocation failed */
+    MUON_ERR_HIP = 5           /* a HIP runtime call or launch failed; see muon_last_error */
+} muon_status;
+
+typedef enum muon_dtype {
+    MUON_BF16 = 0,             /* bfloat16 storage */
+    MUON_F32 = 1               /* float32 storage */
+} muon_dtype;
+
+typedef enum muon_compute {
+    MUON_COMPUTE_BF16 = 0,     /* bf16 MFMA operands, fp32 accumulation, fp32 master X */
+    MUON_COMPUTE_FP32 = 1      /* fp32 MFMA operands and storage: validation mode */
+} muon_compute;
+
+/* init flags */
+#define MUON_INIT_PROFILE     0x1u   /* time every kernel launch with HIP events */
+#define MUON_INIT_FAIL_ALLOC  0x2u   /* test hook: every workspace allocation fails (MUON_ERR_OOM) */
+
+/* One weight matrix of the list handed to muon_step. */
+typedef struct muon_matrix {
+    void       *param;         /* rows x cols, `dtype`, updated in place */
+    const void *grad;          /* rows x cols, `dtype`, read only */
+    float      *momentum;      /* rows x cols float32, updated in place (start at 0) */
+    float      *update_out;    /* optional rows x cols float32: receives O (validation); may be NULL */
+    int64_t     rows, cols;    /* stored shape, both >= 1 */
+    int64_t     ld_param, ld_grad, ld_mom, ld_update;   /* leading dims, elements, >= cols */
+    int32_t     dtype;         /* muon_dtype of param and grad */
+    int32_t     reserved;      /* must be 0 */
+} muon_matrix;
+
+/* Hyperparameters, shared by every matrix of one call. */
+typedef struct muon_hparams {
+    float   lr;                /* learning rate */
+    float   beta;              /* momentum, 0.95 on the pages */
+    float   weight_decay;      /* decoupled: W *= 1 - lr * weight_decay */
+    float   eps;               /* added to the Frobenius norm, 1e-7 on the pages */
+    float   a, b, c;           /* quintic coefficients, (3.4445, -4.7750, 2.0315) */
+    int32_t nesterov;          /* 0 or 1 */
+    int32_t ns_steps;          /* 0..64; 5 on the pages */
+    int32_t compute;           /* muon_compute */
+} muon_hparams;
+
+typedef struct muon_handle muon_handle;
+
+/* Per-kernel launch statistics gathered when the handle was created with MUON_INIT_PROFILE. */
+typedef struct muon_kernel_stats {
+    char    name[48];          /* kernel role: "momentum_norm", "ns_gram", ... */
+    int64_t launches;          /* completed launches timed */
+    double  total_ms;          /* summed HIP-event durations */
+} muon_kernel_stats;
+
+/* Version of this header the library was built from (MUON_ABI_VERSION). */
+int muon_abi_version(void);
+
+/* Create a handle on HIP device `device`.  *out receives the handle (NULL on error).
+ * Errors: MUON_ERR_INVALID_ARG (out == NULL, device out of range, unknown flag bits),
+ * MUON_ERR_NO_DEVICE (no HIP device visible). */
+muon_status muon_init(muon_handle **out, int device, uint32_t flags);
+
+/* One Muon step over `n_mats` matrices (all steps above), enqueued on `stream`.
+ * The first call for a given list of shapes/dtypes/compute mode builds a plan and
+ * allocates the workspace (about 10 bytes per weight element in bf16 mode, plus
+ * two min(rows,cols)^2 bf16 squares per matrix); later calls with the same
+ * signature allocate nothing.
+ * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
+ * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
+ * momentum aliasing param or grad, ns_steps outside 0..64, reserved != 0,
+ * n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
+muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
+                      const muon_hparams *hp, void *stream);
+
+/* Newton-Schulz only: out = NS(in) for one rows x cols matrix (normalise,
+ * transpose rule, hp->ns_steps iterations with hp->a/b/c and hp->eps, in
+ * hp->compute precision).  `in` has dtype `in_dtype` and leading dim ld_in;
+ * `out` is rows x cols float32 with leading dim ld_out.  beta, lr, weight_decay
+ * and nesterov are ignored.  Same errors as muon_step. */
+muon_status muon_orthogonalize(muon_handle *h, const void *in, float *out,
+                               int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
+                               int32_t in_dtype, const muon_hparams *hp, void *stream);
+
+/* Frobenius norms ||u||_F of the orthogonalised inputs of the most recent
+ * muon_step, in list order, copied to host memory `out` (n entries; the call
+ * synchronises the stream).  Validation hook. */
+muon_status muon_read_norms(muon_handle *h, float *out, int32_t n, void *stream);
+
+/* Statistics per kernel role (profiling handles only); returns the number of
+ * entries written (<= max), after waiting for the timed launches to finish. */
+int32_t muon_kernel_stats_read(muon_handle *h, muon_kernel_stats *out, int32_t max);
+void muon_kernel_stats_reset(muon_handle *h);
+
+/* Workspace bytes currently held by the handle. */
+int64_t muon_workspace_bytes(const muon_handle *h);
+
+/* Free the handle and its workspace (waits for the device).  NULL is a no-op. */
+muon_status muon_destroy(muon_handle *h);
+
+/* Static text for a status code. */
+const char *muon_status_str(muon_status s);
+
+/* Text of the last error on this handle ("" if none); valid until the next call. */
+const char *muon_last_error(const muon_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,41 @@
+"""MI355X (gfx950) Muon optimizer step behind a C ABI.
+
+The computation lives in ``libmuon_mi355x.so`` (hand-written HIP kernels);
+this package is its thin ctypes binding.  PyTorch supplies device memory and
+streams only.
+"""
+
+from ._abi import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    LIB_PATH,
+    MUON_BF16,
+    MUON_COMPUTE_BF16,
+    MUON_COMPUTE_FP32,
+    MUON_ERR_DTYPE,
+    MUON_ERR_HIP,
+    MUON_ERR_INVALID_ARG,
+    MUON_ERR_NO_DEVICE,
+    MUON_ERR_OOM,
+    MUON_F32,
+    MUON_INIT_FAIL_ALLOC,
+    MUON_INIT_PROFILE,
+    MUON_OK,
+    Hparams,
+    MuonError,
+    load,
+    make_matrix,
+    muon_abi_version,
+    muon_destroy,
+    muon_init,
+    muon_kernel_stats_read,
+    muon_kernel_stats_reset,
+    muon_last_error,
+    muon_matrix,
+    muon_orthogonalize,
+    muon_read_norms,
+    muon_status_str,
+    muon_step,
+    muon_step_raw,
+    muon_workspace_bytes,
+    muon_hparams,
+)

@@ -1,0 +1,257 @@
+"""ctypes binding of the Muon C ABI (``include/muon.h``).
+
+Argument marshalling only: tensors become device pointers, leading dimensions
+and dtype codes; every step of the computation runs in the HIP library.  The
+library must be built (``newton_schulz_matrix_step_amd._build.build()``); if it
+is missing, loading raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_mi355x.so")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = 1
+MUON_ERR_DTYPE = 2
+MUON_ERR_NO_DEVICE = 3
+MUON_ERR_OOM = 4
+MUON_ERR_HIP = 5
+
+MUON_BF16 = 0
+MUON_F32 = 1
+MUON_COMPUTE_BF16 = 0
+MUON_COMPUTE_FP32 = 1
+
+MUON_INIT_PROFILE = 0x1
+MUON_INIT_FAIL_ALLOC = 0x2
+
+EXPORTED_SYMBOLS = (
+    "muon_abi_version",
+    "muon_init",
+    "muon_step",
+    "muon_orthogonalize",
+    "muon_read_norms",
+    "muon_kernel_stats_read",
+    "muon_kernel_stats_reset",
+    "muon_workspace_bytes",
+    "muon_destroy",
+    "muon_status_str",
+    "muon_last_error",
+)
+
+
+class muon_matrix(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("momentum", ctypes.c_void_p),
+        ("update_out", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("ld_param", ctypes.c_int64),
+        ("ld_grad", ctypes.c_int64),
+        ("ld_mom", ctypes.c_int64),
+        ("ld_update", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class muon_hparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("a", ctypes.c_float),
+        ("b", ctypes.c_float),
+        ("c", ctypes.c_float),
+        ("nesterov", ctypes.c_int32),
+        ("ns_steps", ctypes.c_int32),
+        ("compute", ctypes.c_int32),
+    ]
+
+
+class muon_kernel_stats(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)}: {msg}" if msg else status_str(status))
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"Muon HIP library not built: {path} is missing "
+                          "(run newton_schulz_matrix_step_amd._build.build())")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.muon_abi_version.restype = ctypes.c_int
+    lib.muon_abi_version.argtypes = []
+    lib.muon_init.restype = ctypes.c_int
+    lib.muon_init.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_uint32]
+    lib.muon_step.restype = ctypes.c_int
+    lib.muon_step.argtypes = [vp, ctypes.POINTER(muon_matrix), i32, ctypes.POINTER(muon_hparams), vp]
+    lib.muon_orthogonalize.restype = ctypes.c_int
+    lib.muon_orthogonalize.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(muon_hparams), vp]
+    lib.muon_read_norms.restype = ctypes.c_int
+    lib.muon_read_norms.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32, vp]
+    lib.muon_kernel_stats_read.restype = i32
+    lib.muon_kernel_stats_read.argtypes = [vp, ctypes.POINTER(muon_kernel_stats), i32]
+    lib.muon_kernel_stats_reset.restype = None
+    lib.muon_kernel_stats_reset.argtypes = [vp]
+    lib.muon_workspace_bytes.restype = i64
+    lib.muon_workspace_bytes.argtypes = [vp]
+    lib.muon_destroy.restype = ctypes.c_int
+    lib.muon_destroy.argtypes = [vp]
+    lib.muon_status_str.restype = ctypes.c_char_p
+    lib.muon_status_str.argtypes = [ctypes.c_int]
+    lib.muon_last_error.restype = ctypes.c_char_p
+    lib.muon_last_error.argtypes = [vp]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().muon_status_str(int(status)).decode()
+
+
+def _check(handle, status: int) -> None:
+    if status != MUON_OK:
+        msg = load().muon_last_error(handle).decode() if handle else ""
+        raise MuonError(status, msg)
+
+
+@dataclass
+class Hparams:
+    lr: float = 0.02
+    beta: float = 0.95
+    weight_decay: float = 0.0
+    eps: float = 1e-7
+    a: float = 3.4445
+    b: float = -4.7750
+    c: float = 2.0315
+    nesterov: bool = False
+    ns_steps: int = 5
+    compute: str = "bf16"      # "bf16" or "fp32"
+
+    def to_c(self) -> muon_hparams:
+        comp = {"bf16": MUON_COMPUTE_BF16, "fp32": MUON_COMPUTE_FP32}.get(self.compute, -1)
+        return muon_hparams(self.lr, self.beta, self.weight_decay, self.eps, self.a, self.b, self.c,
+                            int(bool(self.nesterov)), int(self.ns_steps), comp)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    if t.dtype == torch.float32:
+        return MUON_F32
+    return -1
+
+
+def _ld(t) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("matrices must be 2-D with unit column stride")
+    return int(t.stride(0))
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def muon_abi_version() -> int:
+    return int(load().muon_abi_version())
+
+
+def muon_init(device: int = 0, flags: int = 0) -> int:
+    h = ctypes.c_void_p()
+    st = load().muon_init(ctypes.byref(h), int(device), int(flags))
+    _check(None, st)
+    return h.value
+
+
+def make_matrix(param, grad, momentum, update_out=None) -> muon_matrix:
+    """Describe one weight's tensors (device tensors, unit column stride)."""
+    return muon_matrix(
+        param.data_ptr(), grad.data_ptr(), momentum.data_ptr(),
+        update_out.data_ptr() if update_out is not None else None,
+        int(param.shape[0]), int(param.shape[1]),
+        _ld(param), _ld(grad), _ld(momentum), _ld(update_out) if update_out is not None else 0,
+        _dtype_code(param) if _dtype_code(param) == _dtype_code(grad) else -1, 0)
+
+
+def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp: Hparams,
+              update_outs: Optional[Sequence] = None, stream=None) -> None:
+    """One Muon step over every (param, grad, momentum) triple, on ``stream``."""
+    n = len(params)
+    if len(grads) != n or len(moms) != n or (update_outs is not None and len(update_outs) != n):
+        raise ValueError("params, grads, moms (and update_outs) must have the same length")
+    arr = (muon_matrix * max(n, 1))()
+    for i in range(n):
+        arr[i] = make_matrix(params[i], grads[i], moms[i], update_outs[i] if update_outs is not None else None)
+    c_hp = hp.to_c()
+    st = load().muon_step(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream))
+    _check(handle, st)
+
+
+def muon_step_raw(handle: int, arr, n: int, hp: muon_hparams, stream_ptr: int) -> int:
+    """Call with prepared ctypes arguments (the benchmark's inner loop); returns the status."""
+    return load().muon_step(handle, arr, n, ctypes.byref(hp), stream_ptr)
+
+
+def muon_orthogonalize(handle: int, inp, out, hp: Hparams, stream=None) -> None:
+    """out (float32, same shape) = Newton-Schulz(inp)."""
+    c_hp = hp.to_c()
+    st = load().muon_orthogonalize(handle, inp.data_ptr(), out.data_ptr(), int(inp.shape[0]), int(inp.shape[1]),
+                                   _ld(inp), _ld(out), _dtype_code(inp), ctypes.byref(c_hp), _stream_ptr(stream))
+    _check(handle, st)
+
+
+def muon_read_norms(handle: int, n: int, stream=None) -> List[float]:
+    buf = (ctypes.c_float * max(n, 1))()
+    _check(handle, load().muon_read_norms(handle, buf, int(n), _stream_ptr(stream)))
+    return [float(buf[i]) for i in range(n)]
+
+
+def muon_kernel_stats_read(handle: int) -> dict:
+    buf = (muon_kernel_stats * 16)()
+    k = load().muon_kernel_stats_read(handle, buf, 16)
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(k)}
+
+
+def muon_kernel_stats_reset(handle: int) -> None:
+    load().muon_kernel_stats_reset(handle)
+
+
+def muon_workspace_bytes(handle: int) -> int:
+    return int(load().muon_workspace_bytes(handle))
+
+
+def muon_destroy(handle: int) -> None:
+    _check(None, load().muon_destroy(handle))
+
+
+def muon_status_str(status: int) -> str:
+    return status_str(status)
+
+
+def muon_last_error(handle: int) -> str:
+    return load().muon_last_error(handle).decode()

@@ -1,0 +1,556 @@
+// Host side of the Muon C ABI: argument validation, the grouping planner
+// (workspace layout, momentum units, tile lists), descriptor upload and the
+// launch sequence of one step.
+//
+// One step = momentum pass + norm finalize + ns_steps x (GRAM, POLY, AXPY)
+// launches, each launch covering every matrix of the call.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.hpp"
+
+using namespace muon;
+
+namespace {
+
+enum KernelRole {
+    K_MOMENTUM = 0,
+    K_FINALIZE,
+    K_GRAM,
+    K_POLY,
+    K_AXPY,
+    K_AXPY_LAST,
+    K_DIRECT,
+    K_FILL,
+    K_NROLES
+};
+const char* const kRoleNames[K_NROLES] = {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
+                                          "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero"};
+
+constexpr int kStageSlots = 4;
+constexpr int kMaxNsSteps = 64;
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+    bool valid = false;
+    std::vector<int64_t> key;
+    int n = 0;
+    bool f32c = false;
+    std::vector<MatDesc> geom;     // static part of every descriptor
+    std::vector<MatDesc> uploaded; // last descriptor table sent to the device
+    bool have_uploaded = false;
+    MatDesc* d_desc = nullptr;
+    Tile* d_gram = nullptr;
+    int n_gram = 0;
+    Tile* d_axpy = nullptr;
+    int n_axpy = 0;
+    Unit* d_units = nullptr;
+    int n_units = 0;
+    float* d_partials = nullptr;
+    float* d_inv = nullptr;
+    float* d_nu = nullptr;
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    MatDesc* h_stage[kStageSlots] = {};
+    hipEvent_t stage_ev[kStageSlots] = {};
+    bool stage_used[kStageSlots] = {};
+    int slot = 0;
+};
+
+struct Pending {
+    int role;
+    hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct muon_handle {
+    int device = 0;
+    uint32_t flags = 0;
+    std::string err;
+    Plan step_plan, ortho_plan;
+    bool profile = false;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> ev_pool;
+    int64_t launches[K_NROLES] = {};
+    double total_ms[K_NROLES] = {};
+};
+
+namespace {
+
+muon_status fail(muon_handle* h, muon_status st, const char* fmt, ...) {
+    if (h) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof buf, fmt, ap);
+        va_end(ap);
+        h->err = buf;
+    }
+    return st;
+}
+
+muon_status hip_fail(muon_handle* h, hipError_t e, const char* what) {
+    return fail(h, MUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int old = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&old) != hipSuccess) old = -1;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (old >= 0) (void)hipSetDevice(old);
+    }
+};
+
+void free_plan(Plan& p) {
+    (void)hipFree(p.d_desc);
+    (void)hipFree(p.d_gram);
+    (void)hipFree(p.d_axpy);
+    (void)hipFree(p.d_units);
+    (void)hipFree(p.d_partials);
+    (void)hipFree(p.d_inv);
+    (void)hipFree(p.d_nu);
+    (void)hipFree(p.ws);
+    for (int i = 0; i < kStageSlots; ++i) {
+        if (p.stage_ev[i]) (void)hipEventDestroy(p.stage_ev[i]);
+        if (p.h_stage[i]) (void)hipHostFree(p.h_stage[i]);
+    }
+    p = Plan();
+}
+
+// Everything a caller passes for one matrix, before validation.
+struct MatIn {
+    void* param;
+    const void* grad;
+    float* mom;
+    float* upd;
+    int64_t R, C, ld_param, ld_grad, ld_mom, ld_upd;
+    int32_t dtype;
+    bool has_param, has_mom;
+};
+
+muon_status validate_hp(muon_handle* h, const muon_hparams* hp) {
+    if (!hp) return fail(h, MUON_ERR_INVALID_ARG, "hparams is NULL");
+    if (hp->compute != MUON_COMPUTE_BF16 && hp->compute != MUON_COMPUTE_FP32)
+        return fail(h, MUON_ERR_DTYPE, "unknown compute mode %d", hp->compute);
+    if (hp->ns_steps < 0 || hp->ns_steps > kMaxNsSteps)
+        return fail(h, MUON_ERR_INVALID_ARG, "ns_steps %d outside 0..%d", hp->ns_steps, kMaxNsSteps);
+    if (hp->nesterov != 0 && hp->nesterov != 1)
+        return fail(h, MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1, got %d", hp->nesterov);
+    return MUON_OK;
+}
+
+muon_status validate_mat(muon_handle* h, const MatIn& m, int idx) {
+    if (m.dtype != MUON_BF16 && m.dtype != MUON_F32) return fail(h, MUON_ERR_DTYPE, "matrix %d: unknown dtype %d", idx, m.dtype);
+    if (!m.grad) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: grad/input is NULL", idx);
+    if (m.has_param && !m.param) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: param is NULL", idx);
+    if (m.has_mom && !m.mom) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: momentum is NULL", idx);
+    if (!m.has_param && !m.upd) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: output is NULL", idx);
+    if (m.R < 1 || m.C < 1 || m.R > kMaxDim || m.C > kMaxDim || m.R * m.C > kMaxElems)
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: bad shape %lld x %lld", idx, (long long)m.R, (long long)m.C);
+    if (m.ld_grad < m.C || (m.has_param && m.ld_param < m.C) || (m.has_mom && m.ld_mom < m.C) ||
+        (m.upd && m.ld_upd < m.C))
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: leading dimension smaller than cols", idx);
+    if (m.ld_grad > kMaxElems || m.ld_param > kMaxElems || m.ld_mom > kMaxElems || m.ld_upd > kMaxElems)
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: leading dimension too large", idx);
+    const void* g = m.grad;
+    if (m.has_param && m.param == g) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: param aliases grad", idx);
+    if (m.has_mom && (static_cast<const void*>(m.mom) == g || static_cast<void*>(m.mom) == m.param))
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: momentum aliases param or grad", idx);
+    if (m.upd && (static_cast<const void*>(m.upd) == g || static_cast<void*>(m.upd) == m.param ||
+                  (m.has_mom && m.upd == m.mom)))
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: update_out aliases another buffer", idx);
+    return MUON_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Static geometry, workspace layout, units and tiles for one call signature.
+muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, bool f32c,
+                       const std::vector<int64_t>& key, hipStream_t stream) {
+    if (p.valid || p.ws) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize before re-plan");
+        free_plan(p);
+    }
+    const int n = int(mats.size());
+    const int64_t es = f32c ? 4 : 2;
+    std::vector<MatDesc> geom(n);
+    std::vector<Unit> units;
+    std::vector<Tile> gram, axpy;
+    size_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const size_t o = off;
+        off += size_t(round_up(bytes, 256));
+        return int64_t(o);
+    };
+    for (int i = 0; i < n; ++i) {
+        const MatIn& m = mats[i];
+        MatDesc d;
+        std::memset(&d, 0, sizeof d);
+        d.R = int32_t(m.R);
+        d.C = int32_t(m.C);
+        d.trans = m.R > m.C;
+        d.m = int32_t(std::min(m.R, m.C));
+        d.n = int32_t(std::max(m.R, m.C));
+        d.Rp = int32_t(round_up(m.R, kPad));
+        d.Cp = int32_t(round_up(m.C, kPad));
+        d.mp = int32_t(round_up(d.m, kPad));
+        d.np = int32_t(round_up(d.n, kPad));
+        d.io_dtype = m.dtype;
+        d.has_param = m.has_param;
+        d.has_mom = m.has_mom;
+        d.shape_scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));
+        const int64_t xe = int64_t(d.mp) * d.np;
+        d.off_u = take(int64_t(d.Rp) * d.Cp * es);
+        d.off_xm = f32c ? 0 : take(xe * 4);
+        d.off_xb0 = take(xe * es);
+        d.off_xb1 = take(xe * es);
+        d.off_a = take(int64_t(d.mp) * d.mp * es);
+        d.off_b = take(int64_t(d.mp) * d.mp * es);
+        // momentum-pass units: whole rows, about kUnitElems elements each
+        const int rows_per_unit = int(std::max<int64_t>(1, kUnitElems / m.C));
+        d.unit0 = int32_t(units.size());
+        for (int64_t r = 0; r < m.R; r += rows_per_unit)
+            units.push_back(Unit{i, int32_t(r), int32_t(std::min<int64_t>(m.R, r + rows_per_unit)), 0});
+        d.nunits = int32_t(units.size()) - d.unit0;
+        // Newton-Schulz tiles: upper triangle of the m x m products, full m x n grid
+        const int tm = (d.m + kTile - 1) / kTile, tn = (d.n + kTile - 1) / kTile;
+        for (int a = 0; a < tm; ++a)
+            for (int b = a; b < tm; ++b) gram.push_back(Tile{i, a, b, 0});
+        for (int a = 0; a < tm; ++a)
+            for (int b = 0; b < tn; ++b) axpy.push_back(Tile{i, a, b, 0});
+        geom[i] = d;
+    }
+
+    if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "workspace allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
+
+    Plan q;
+    auto dmalloc = [&](void** ptr, size_t bytes) -> bool {
+        return hipMalloc(ptr, std::max<size_t>(bytes, 16)) == hipSuccess;
+    };
+    bool ok = dmalloc(reinterpret_cast<void**>(&q.d_desc), sizeof(MatDesc) * n) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_gram), sizeof(Tile) * gram.size()) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_axpy), sizeof(Tile) * axpy.size()) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_units), sizeof(Unit) * units.size()) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_partials), sizeof(float) * units.size()) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_inv), sizeof(float) * n) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_nu), sizeof(float) * n) &&
+              dmalloc(reinterpret_cast<void**>(&q.ws), off);
+    for (int i = 0; ok && i < kStageSlots; ++i) {
+        ok = hipHostMalloc(reinterpret_cast<void**>(&q.h_stage[i]), sizeof(MatDesc) * std::max(n, 1), hipHostMallocDefault) == hipSuccess &&
+             hipEventCreateWithFlags(&q.stage_ev[i], hipEventDisableTiming) == hipSuccess;
+    }
+    if (!ok) {
+        (void)hipGetLastError();
+        free_plan(q);
+        return fail(h, MUON_ERR_OOM, "workspace allocation of %.3f GB failed", double(off) / 1e9);
+    }
+    q.ws_bytes = off;
+    hipError_t e = launch_fill_zero(q.ws, off, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(q.d_gram, gram.data(), sizeof(Tile) * gram.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(q.d_axpy, axpy.data(), sizeof(Tile) * axpy.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(q.d_units, units.data(), sizeof(Unit) * units.size(), hipMemcpyHostToDevice, stream);
+    // the host vectors die with this call: wait for the copies
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) {
+        free_plan(q);
+        return hip_fail(h, e, "plan upload");
+    }
+    q.n = n;
+    q.f32c = f32c;
+    q.geom = std::move(geom);
+    q.n_gram = int(gram.size());
+    q.n_axpy = int(axpy.size());
+    q.n_units = int(units.size());
+    q.key = key;
+    q.valid = true;
+    p = std::move(q);
+    return MUON_OK;
+}
+
+hipEvent_t get_event(muon_handle* h) {
+    if (!h->ev_pool.empty()) {
+        hipEvent_t e = h->ev_pool.back();
+        h->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(muon_handle* h, int role, hipStream_t s, F&& launch) {
+    if (!h->profile) return launch();
+    hipEvent_t a = get_event(h), b = get_event(h);
+    if (!a || !b) return launch();
+    hipError_t e = hipEventRecord(a, s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(b, s);
+    if (e == hipSuccess) h->pending.push_back(Pending{role, a, b});
+    return e;
+}
+
+muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream) {
+    const int n = int(mats.size());
+    const bool f32c = hp->compute == MUON_COMPUTE_FP32;
+    std::vector<int64_t> key;
+    key.reserve(2 + 5 * size_t(n));
+    key.push_back(n);
+    key.push_back(f32c);
+    for (const MatIn& m : mats) {
+        key.push_back(m.R);
+        key.push_back(m.C);
+        key.push_back(m.dtype);
+        key.push_back(m.has_param);
+        key.push_back(m.has_mom);
+    }
+    if (!plan.valid || plan.key != key) {
+        muon_status st = build_plan(h, plan, mats, f32c, key, stream);
+        if (st != MUON_OK) return st;
+    }
+
+    // descriptor table: static geometry + this call's pointers
+    std::vector<MatDesc> desc(plan.geom);
+    for (int i = 0; i < n; ++i) {
+        const MatIn& m = mats[i];
+        MatDesc& d = desc[i];
+        d.param = m.param;
+        d.grad = m.grad;
+        d.mom = m.mom;
+        d.upd = m.upd;
+        d.ld_param = m.ld_param;
+        d.ld_grad = m.ld_grad;
+        d.ld_mom = m.ld_mom;
+        d.ld_upd = m.ld_upd;
+        d.vec_ok = (m.C % 8 == 0) && (m.ld_grad % 8 == 0) && aligned16(m.grad) &&
+                   (!m.has_mom || ((m.ld_mom % 8 == 0) && aligned16(m.mom)));
+    }
+    hipError_t e;
+    if (!plan.have_uploaded || std::memcmp(desc.data(), plan.uploaded.data(), sizeof(MatDesc) * n) != 0) {
+        const int s = plan.slot;
+        if (plan.stage_used[s]) {
+            e = hipEventSynchronize(plan.stage_ev[s]);
+            if (e != hipSuccess) return hip_fail(h, e, "descriptor staging wait");
+        }
+        std::memcpy(plan.h_stage[s], desc.data(), sizeof(MatDesc) * n);
+        e = hipMemcpyAsync(plan.d_desc, plan.h_stage[s], sizeof(MatDesc) * n, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipEventRecord(plan.stage_ev[s], stream);
+        if (e != hipSuccess) return hip_fail(h, e, "descriptor upload");
+        plan.stage_used[s] = true;
+        plan.slot = (s + 1) % kStageSlots;
+        plan.uploaded = desc;
+        plan.have_uploaded = true;
+    }
+
+    MomentumArgs ma;
+    ma.ws = plan.ws;
+    ma.partials = plan.d_partials;
+    ma.beta = hp->beta;
+    ma.nesterov = hp->nesterov;
+    e = timed(h, K_MOMENTUM, stream, [&] { return launch_momentum(plan.d_units, plan.n_units, plan.d_desc, ma, f32c, stream); });
+    if (e != hipSuccess) return hip_fail(h, e, "momentum launch");
+    e = timed(h, K_FINALIZE, stream, [&] {
+        return launch_finalize_norm(plan.d_desc, n, plan.d_partials, plan.d_inv, plan.d_nu, hp->eps, stream);
+    });
+    if (e != hipSuccess) return hip_fail(h, e, "norm launch");
+
+    PhaseArgs pa;
+    pa.ws = plan.ws;
+    pa.inv_norm = plan.d_inv;
+    pa.a = hp->a;
+    pa.b = hp->b;
+    pa.c = hp->c;
+    pa.lr = hp->lr;
+    pa.wd = hp->weight_decay;
+    pa.beta = hp->beta;
+    pa.nesterov = hp->nesterov;
+    pa.iter = 0;
+    if (hp->ns_steps == 0) {
+        e = timed(h, K_DIRECT, stream, [&] { return launch_direct_update(plan.d_units, plan.n_units, plan.d_desc, pa, stream); });
+        if (e != hipSuccess) return hip_fail(h, e, "update launch");
+        return MUON_OK;
+    }
+    for (int it = 1; it <= hp->ns_steps; ++it) {
+        pa.iter = it;
+        e = timed(h, K_GRAM, stream, [&] { return launch_ns_phase(PH_GRAM, f32c, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        if (e != hipSuccess) return hip_fail(h, e, "gram launch");
+        e = timed(h, K_POLY, stream, [&] { return launch_ns_phase(PH_POLY, f32c, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        if (e != hipSuccess) return hip_fail(h, e, "poly launch");
+        const bool last = it == hp->ns_steps;
+        e = timed(h, last ? K_AXPY_LAST : K_AXPY, stream, [&] {
+            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.d_axpy, plan.n_axpy, plan.d_desc, pa, stream);
+        });
+        if (e != hipSuccess) return hip_fail(h, e, "axpy launch");
+    }
+    return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
+    if (!out) return MUON_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC)) return MUON_ERR_INVALID_ARG;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return MUON_ERR_NO_DEVICE;
+    }
+    if (device < 0 || device >= count) return MUON_ERR_INVALID_ARG;
+    muon_handle* h = new (std::nothrow) muon_handle();
+    if (!h) return MUON_ERR_OOM;
+    h->device = device;
+    h->flags = flags;
+    h->profile = (flags & MUON_INIT_PROFILE) != 0;
+    *out = h;
+    return MUON_OK;
+}
+
+muon_status muon_step(muon_handle* h, const muon_matrix* mats, int32_t n_mats, const muon_hparams* hp, void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    h->err.clear();
+    if (n_mats < 0) return fail(h, MUON_ERR_INVALID_ARG, "n_mats %d < 0", n_mats);
+    if (n_mats == 0) return MUON_OK;
+    if (!mats) return fail(h, MUON_ERR_INVALID_ARG, "mats is NULL");
+    muon_status st = validate_hp(h, hp);
+    if (st != MUON_OK) return st;
+    std::vector<MatIn> in(n_mats);
+    for (int i = 0; i < n_mats; ++i) {
+        const muon_matrix& m = mats[i];
+        if (m.reserved != 0) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: reserved field must be 0", i);
+        in[i] = MatIn{m.param, m.grad, m.momentum, m.update_out, m.rows, m.cols, m.ld_param,
+                      m.ld_grad, m.ld_mom, m.update_out ? m.ld_update : 0, m.dtype, true, true};
+        st = validate_mat(h, in[i], i);
+        if (st != MUON_OK) return st;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
+    return run(h, h->step_plan, in, hp, static_cast<hipStream_t>(stream));
+}
+
+muon_status muon_orthogonalize(muon_handle* h, const void* in, float* out, int64_t rows, int64_t cols, int64_t ld_in,
+                               int64_t ld_out, int32_t in_dtype, const muon_hparams* hp, void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    h->err.clear();
+    muon_status st = validate_hp(h, hp);
+    if (st != MUON_OK) return st;
+    if (!out) return fail(h, MUON_ERR_INVALID_ARG, "out is NULL");
+    if (in == static_cast<const void*>(out)) return fail(h, MUON_ERR_INVALID_ARG, "in aliases out");
+    std::vector<MatIn> m(1);
+    m[0] = MatIn{nullptr, in, nullptr, out, rows, cols, 0, ld_in, 0, ld_out, in_dtype, false, false};
+    st = validate_mat(h, m[0], 0);
+    if (st != MUON_OK) return st;
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
+    return run(h, h->ortho_plan, m, hp, static_cast<hipStream_t>(stream));
+}
+
+muon_status muon_read_norms(muon_handle* h, float* out, int32_t n, void* stream) {
+    if (!h || !out || n < 0) return MUON_ERR_INVALID_ARG;
+    if (!h->step_plan.valid || n > h->step_plan.n) return fail(h, MUON_ERR_INVALID_ARG, "no step with %d matrices yet", n);
+    if (n == 0) return MUON_OK;
+    DeviceGuard g(h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(out, h->step_plan.d_nu, sizeof(float) * n, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(h, e, "norm readback");
+    return MUON_OK;
+}
+
+int32_t muon_kernel_stats_read(muon_handle* h, muon_kernel_stats* out, int32_t max) {
+    if (!h) return 0;
+    DeviceGuard g(h->device);
+    for (const Pending& p : h->pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            h->launches[p.role] += 1;
+            h->total_ms[p.role] += ms;
+        }
+        h->ev_pool.push_back(p.a);
+        h->ev_pool.push_back(p.b);
+    }
+    h->pending.clear();
+    int32_t k = 0;
+    for (int r = 0; r < K_NROLES && out && k < max; ++r) {
+        if (h->launches[r] == 0) continue;
+        std::memset(&out[k], 0, sizeof(muon_kernel_stats));
+        std::snprintf(out[k].name, sizeof out[k].name, "%s", kRoleNames[r]);
+        out[k].launches = h->launches[r];
+        out[k].total_ms = h->total_ms[r];
+        ++k;
+    }
+    return k;
+}
+
+void muon_kernel_stats_reset(muon_handle* h) {
+    if (!h) return;
+    (void)muon_kernel_stats_read(h, nullptr, 0);
+    for (int r = 0; r < K_NROLES; ++r) {
+        h->launches[r] = 0;
+        h->total_ms[r] = 0.0;
+    }
+}
+
+int64_t muon_workspace_bytes(const muon_handle* h) {
+    if (!h) return 0;
+    return int64_t(h->step_plan.ws_bytes + h->ortho_plan.ws_bytes);
+}
+
+muon_status muon_destroy(muon_handle* h) {
+    if (!h) return MUON_OK;
+    {
+        DeviceGuard g(h->device);
+        (void)hipDeviceSynchronize();
+        free_plan(h->step_plan);
+        free_plan(h->ortho_plan);
+        for (const Pending& p : h->pending) {
+            (void)hipEventDestroy(p.a);
+            (void)hipEventDestroy(p.b);
+        }
+        for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
+    }
+    delete h;
+    return MUON_OK;
+}
+
+const char* muon_status_str(muon_status s) {
+    switch (s) {
+        case MUON_OK: return "MUON_OK";
+        case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG";
+        case MUON_ERR_DTYPE: return "MUON_ERR_DTYPE";
+        case MUON_ERR_NO_DEVICE: return "MUON_ERR_NO_DEVICE";
+        case MUON_ERR_OOM: return "MUON_ERR_OOM";
+        case MUON_ERR_HIP: return "MUON_ERR_HIP";
+    }
+    return "MUON_ERR_UNKNOWN";
+}
+
+const char* muon_last_error(const muon_handle* h) { return h ? h->err.c_str() : ""; }
+
+}  // extern "C"

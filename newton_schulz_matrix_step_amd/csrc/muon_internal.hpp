@@ -1,0 +1,83 @@
+// Internal descriptors shared by the host planner (muon_api.cpp) and the
+// gfx950 kernels (muon_kernels.hip).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// All workspace matrices are padded to multiples of this many rows/columns and
+// zero-filled once, so tile loads never leave the allocation and padding reads
+// contribute zeros to every contraction.
+constexpr int kPad = 256;
+
+// Per-matrix descriptor, one entry per matrix of the call, in device memory.
+// "Stored" = the caller's orientation (R x C); "NS" = the m x n orientation the
+// iteration works in (m = min(R, C) rows, transposed when R > C).
+struct MatDesc {
+    int32_t R, C;              // stored shape
+    int32_t m, n;              // NS shape, m <= n
+    int32_t Rp, Cp;            // padded stored shape (U buffer)
+    int32_t mp, np;            // padded NS shape
+    int32_t trans;             // R > C
+    int32_t io_dtype;          // storage dtype of param / grad / input (0 bf16, 1 f32)
+    int32_t has_param;         // 0 for the orthogonalise-only entry point
+    int32_t has_mom;           // 0: u = g (no momentum buffer)
+    int32_t unit0, nunits;     // momentum-pass units owned by this matrix
+    int32_t vec_ok;            // 16-byte vector path legal for param/grad/mom/upd
+    float shape_scale;         // sqrt(max(1, R / C))
+    int64_t off_u;             // workspace byte offsets
+    int64_t off_xm;            // fp32 master X (bf16 mode only)
+    int64_t off_xb0, off_xb1;  // operand copies of X, ping-pong
+    int64_t off_a, off_b;      // A = X X^T and B = b A + c A^2 (mp x mp)
+    void* param;
+    const void* grad;
+    float* mom;
+    float* upd;
+    int64_t ld_param, ld_grad, ld_mom, ld_upd;
+};
+
+// One work unit of the momentum pass: rows [r0, r1) of matrix `mat`.
+struct Unit {
+    int32_t mat, r0, r1, pad;
+};
+
+// One output tile of a Newton-Schulz product.
+struct Tile {
+    int32_t mat, ti, tj, pad;
+};
+
+enum PhaseKind : int { PH_GRAM = 0, PH_POLY = 1, PH_AXPY = 2, PH_AXPY_LAST = 3 };
+
+struct PhaseArgs {
+    char* ws;
+    const float* inv_norm;     // per matrix 1 / (||u||_F + eps)
+    float a, b, c;
+    float lr, wd, beta;
+    int32_t iter;              // 1-based iteration index
+    int32_t nesterov;
+};
+
+struct MomentumArgs {
+    char* ws;
+    float* partials;           // one sum of squares per unit
+    float beta;
+    int32_t nesterov;
+};
+
+// Launch wrappers (muon_kernels.hip).  All return the launch status.
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a,
+                           bool f32_compute, hipStream_t s);
+hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials,
+                                float* inv_norm, float* nu, float eps, hipStream_t s);
+hipError_t launch_ns_phase(int kind, bool f32_compute, const Tile* tiles, int n_tiles,
+                           const MatDesc* mats, PhaseArgs a, hipStream_t s);
+hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats,
+                                PhaseArgs a, hipStream_t s);
+
+// Tile edge used by the Newton-Schulz GEMMs.
+constexpr int kTile = 128;
+
+}  // namespace muon

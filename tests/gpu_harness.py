@@ -1,0 +1,136 @@
+"""Helpers shared by the GPU tests: upload seeded stored inputs, run the HIP
+path through the C ABI, read results back, compare with the oracle."""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+import oracle
+from muon_synth import Workload, encode_storage, make_grad, make_momentum, make_param
+
+# Parity bars (rel-F = ||x - y||_F / ||y||_F against the float64 oracle).
+TOL_O_BF16 = 3e-2        # orthogonalised update, bf16 MFMA mode
+TOL_O_FP32 = 1e-5        # orthogonalised update, fp32 validation mode
+TOL_MOM = 1e-6           # momentum buffers, fp32 storage
+
+
+def relf(x: np.ndarray, y: np.ndarray) -> float:
+    d = np.linalg.norm(np.asarray(x, np.float64) - np.asarray(y, np.float64))
+    return float(d / max(np.linalg.norm(np.asarray(y, np.float64)), 1e-300))
+
+
+def to_device(stored: np.ndarray, dev="cuda"):
+    import torch
+    if stored.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(stored).view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(stored, dtype=np.float32).copy()).to(dev)
+
+
+def to_stored(t) -> np.ndarray:
+    """Device tensor -> stored numpy representation (uint16 bf16 bits or float32)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().contiguous().cpu().numpy().astype(np.float32)
+
+
+def bf16_rne_from_f64(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 with one rounding (nearest, ties to even); uint16 bits.
+    Used only to state the expected stored weight from float64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2^e, 0.5 <= |m| < 1
+    q = np.round(m * 256.0) / 256.0          # 8 significant bits, numpy rounds half to even
+    y = np.ldexp(q, e).astype(np.float32)    # exact in float32
+    return (y.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|ordinal(a) - ordinal(b)| for bf16 bit patterns (sign-magnitude to ordinal)."""
+    def ordinal(u):
+        u = u.astype(np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordinal(a) - ordinal(b))
+
+
+def hparams_for(wl: Workload):
+    import newton_schulz_matrix_step_amd as nsm
+    return nsm.Hparams(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
+                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute)
+
+
+def oracle_hyper(wl: Workload) -> oracle.Hyper:
+    return oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
+                        ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c)
+
+
+@dataclass
+class StepRecord:
+    w_old: np.ndarray    # stored representation before the step
+    w_new: np.ndarray    # stored representation after the step
+    m_new: np.ndarray    # float32
+    o: np.ndarray        # float32 update_out
+    g: np.ndarray        # stored gradient of this step
+
+
+def run_gpu(wl: Workload, steps: int, check: Sequence[int], handle=None, grad_fn=None) -> Dict[int, List[StepRecord]]:
+    """Run ``steps`` Muon steps over every matrix of ``wl`` in one grouped call per
+    step; record the matrices listed in ``check``."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    own = handle is None
+    h = nsm.muon_init(0) if own else handle
+    try:
+        n = len(wl.mats)
+        params = [to_device(encode_storage(make_param(wl, i), wl.storage)) for i in range(n)]
+        moms = [to_device(encode_storage(make_momentum(wl, i), "fp32")) for i in range(n)]
+        upd = [torch.empty(m.rows, m.cols, dtype=torch.float32, device="cuda") for m in wl.mats]
+        hp = hparams_for(wl)
+        rec: Dict[int, List[StepRecord]] = {i: [] for i in check}
+        gf = grad_fn or make_grad
+        for s in range(1, steps + 1):
+            g_stored = [encode_storage(gf(wl, s, i), wl.storage) for i in range(n)]
+            grads = [to_device(x) for x in g_stored]
+            w_old = {i: to_stored(params[i]) for i in check}
+            nsm.muon_step(h, params, grads, moms, hp, update_outs=upd)
+            torch.cuda.synchronize()
+            for i in check:
+                rec[i].append(StepRecord(w_old[i], to_stored(params[i]), to_stored(moms[i]), to_stored(upd[i]),
+                                         g_stored[i]))
+        return rec
+    finally:
+        if own:
+            nsm.muon_destroy(h)
+
+
+def check_against_oracle(wl: Workload, rec: Dict[int, List[StepRecord]], tol_o: float, tol_w_f32: float = 1e-5,
+                         report: Optional[list] = None) -> None:
+    """Replay every recorded matrix through the oracle from the same initial state
+    and the same stored gradients; assert the parity bars."""
+    hp = oracle_hyper(wl)
+    for i, steps in rec.items():
+        m = oracle.decode(encode_storage(make_momentum(wl, i), "fp32"))
+        for s, r in enumerate(steps):
+            w_old = oracle.decode(r.w_old)
+            g = oracle.decode(r.g)
+            res = oracle.muon_step_matrix(w_old, g, m, hp)
+            e_m = relf(r.m_new, res.m)
+            e_o = relf(r.o, res.o)
+            if report is not None:
+                report.append((i, s + 1, e_m, e_o))
+            assert e_m <= TOL_MOM, f"matrix {i} step {s + 1}: momentum rel err {e_m:.3e}"
+            assert e_o <= tol_o, f"matrix {i} step {s + 1}: O rel err {e_o:.3e} > {tol_o}"
+            # the stored weight: float64 update of the GPU's own O, rounded once
+            sc = math.sqrt(max(1.0, r.w_old.shape[0] / r.w_old.shape[1]))
+            w_exp = w_old * (1.0 - wl.lr * wl.weight_decay) - wl.lr * sc * r.o.astype(np.float64)
+            if r.w_new.dtype == np.uint16:
+                d = bf16_ulp_distance(r.w_new, bf16_rne_from_f64(w_exp))
+                assert int(d.max()) <= 1, f"matrix {i} step {s + 1}: weight off by {int(d.max())} bf16 ulp"
+            else:
+                dw_gpu = r.w_new.astype(np.float64) - w_old
+                e_w = relf(dw_gpu, res.w - w_old)
+                assert e_w <= max(tol_w_f32, tol_o), f"matrix {i} step {s + 1}: dW rel err {e_w:.3e}"
+            m = res.m  # the oracle keeps its own float64 momentum trajectory

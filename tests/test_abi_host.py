@@ -1,0 +1,94 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point its header declares, agrees with the header on struct
+layouts, and reports a missing device instead of touching one."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import newton_schulz_matrix_step_amd as nsm
+from newton_schulz_matrix_step_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.fail("HIP library not built: run __graft_entry__.build() first")
+    return nsm.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert "muon_step" in declared and "muon_init" in declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in muon.h but not exported"
+    assert sorted(declared) == sorted(_abi.EXPORTED_SYMBOLS)
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define MUON_ABI_VERSION (\d+)", text).group(1))
+    assert nsm.muon_abi_version() == ver
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "muon.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(muon_matrix), sizeof(muon_hparams),"
+        " sizeof(muon_kernel_stats), offsetof(muon_matrix, dtype), offsetof(muon_hparams, ns_steps),"
+        " offsetof(muon_matrix, ld_update)); return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out == [ctypes.sizeof(_abi.muon_matrix), ctypes.sizeof(_abi.muon_hparams),
+                   ctypes.sizeof(_abi.muon_kernel_stats), _abi.muon_matrix.dtype.offset,
+                   _abi.muon_hparams.ns_steps.offset, _abi.muon_matrix.ld_update.offset]
+
+
+def test_status_strings(lib):
+    for code, name in ((0, "MUON_OK"), (1, "MUON_ERR_INVALID_ARG"), (2, "MUON_ERR_DTYPE"),
+                       (3, "MUON_ERR_NO_DEVICE"), (4, "MUON_ERR_OOM"), (5, "MUON_ERR_HIP")):
+        assert nsm.muon_status_str(code) == name
+
+
+def test_null_handle_and_args(lib):
+    hp = nsm.Hparams().to_c()
+    assert lib.muon_step(None, None, 0, ctypes.byref(hp), None) == nsm.MUON_ERR_INVALID_ARG
+    assert lib.muon_orthogonalize(None, None, None, 1, 1, 1, 1, 0, ctypes.byref(hp), None) == nsm.MUON_ERR_INVALID_ARG
+    assert lib.muon_init(None, 0, 0) == nsm.MUON_ERR_INVALID_ARG
+    assert lib.muon_destroy(None) == nsm.MUON_OK
+    assert lib.muon_last_error(None) == b""
+    assert lib.muon_workspace_bytes(None) == 0
+    assert lib.muon_kernel_stats_read(None, None, 0) == 0
+
+
+def test_init_without_gpu_reports_no_device(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    h = ctypes.c_void_p()
+    assert lib.muon_init(ctypes.byref(h), 0, 0) == nsm.MUON_ERR_NO_DEVICE
+    assert h.value is None
+    with pytest.raises(nsm.MuonError) as ei:
+        nsm.muon_init(0)
+    assert ei.value.status == nsm.MUON_ERR_NO_DEVICE
+    assert lib.muon_init(ctypes.byref(h), 0, 0x80) == nsm.MUON_ERR_INVALID_ARG   # unknown flag bits
+
+
+def test_hparams_marshalling():
+    c = nsm.Hparams(lr=0.5, nesterov=True, ns_steps=3, compute="fp32").to_c()
+    assert (c.lr, c.nesterov, c.ns_steps, c.compute) == (0.5, 1, 3, nsm.MUON_COMPUTE_FP32)
+    assert nsm.Hparams(compute="fp16").to_c().compute == -1
