@@ -56,6 +56,23 @@ def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordinal(a) - ordinal(b))
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (normal range)."""
+    return np.spacing(np.abs(np.asarray(x, np.float64)).astype(np.float32)).astype(np.float64) * 65536.0
+
+
+def weight_error_ok(w_new_bits: np.ndarray, w_old: np.ndarray, o: np.ndarray, lr: float, wd: float,
+                    scale: float) -> np.ndarray:
+    """Elementwise: the stored bf16 weight lies within one bf16 ulp of the exact
+    float64 update of the GPU's own O, widened by the float32 evaluation error of
+    W (1 - lr wd) - lr s O (a few float32 roundings of each term), which matters
+    only where the two terms cancel."""
+    w_exp = w_old * (1.0 - lr * wd) - lr * scale * o
+    got = (w_new_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    slack = 4.0 * 2.0 ** -24 * (np.abs(w_old) + lr * scale * np.abs(o))
+    return np.abs(got - w_exp) <= bf16_ulp(w_exp) + slack
+
+
 def hparams_for(wl: Workload):
     import newton_schulz_matrix_step_amd as nsm
     return nsm.Hparams(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
@@ -121,14 +138,15 @@ def check_against_oracle(wl: Workload, rec: Dict[int, List[StepRecord]], tol_o: 
             e_o = relf(r.o, res.o)
             if report is not None:
                 report.append((i, s + 1, e_m, e_o))
+            print(f"  matrix {i} {r.w_old.shape} step {s + 1}: mom {e_m:.2e}  O {e_o:.2e}", flush=True)
             assert e_m <= TOL_MOM, f"matrix {i} step {s + 1}: momentum rel err {e_m:.3e}"
             assert e_o <= tol_o, f"matrix {i} step {s + 1}: O rel err {e_o:.3e} > {tol_o}"
             # the stored weight: float64 update of the GPU's own O, rounded once
             sc = math.sqrt(max(1.0, r.w_old.shape[0] / r.w_old.shape[1]))
             w_exp = w_old * (1.0 - wl.lr * wl.weight_decay) - wl.lr * sc * r.o.astype(np.float64)
             if r.w_new.dtype == np.uint16:
-                d = bf16_ulp_distance(r.w_new, bf16_rne_from_f64(w_exp))
-                assert int(d.max()) <= 1, f"matrix {i} step {s + 1}: weight off by {int(d.max())} bf16 ulp"
+                ok = weight_error_ok(r.w_new, w_old, r.o.astype(np.float64), wl.lr, wl.weight_decay, sc)
+                assert ok.all(), f"matrix {i} step {s + 1}: {int((~ok).sum())} weights beyond 1 bf16 ulp"
             else:
                 dw_gpu = r.w_new.astype(np.float64) - w_old
                 e_w = relf(dw_gpu, res.w - w_old)

@@ -86,10 +86,9 @@ def test_zero_gradient_and_zero_lr():
         nsm.muon_step(h, [w], [g], [m], nsm.Hparams(lr=0.02, weight_decay=0.5), update_outs=[o])
         torch.cuda.synchronize()
         assert torch.count_nonzero(o).item() == 0
-        from gpu_harness import bf16_rne_from_f64, bf16_ulp_distance
-        exp = bf16_rne_from_f64(to_stored(w0).astype(np.uint32).__lshift__(16).view(np.float32).astype(np.float64)
-                                * (1 - 0.02 * 0.5))
-        assert int(bf16_ulp_distance(to_stored(w), exp).max()) <= 1
+        from gpu_harness import weight_error_ok
+        w0_64 = (to_stored(w0).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert weight_error_ok(to_stored(w), w0_64, np.zeros_like(w0_64), 0.02, 0.5, 1.0).all()
         g2 = torch.randn(70, 90, device="cuda").to(torch.bfloat16)
         w1 = w.clone()
         nsm.muon_step(h, [w], [g2], [m], nsm.Hparams(lr=0.0, weight_decay=0.5))
