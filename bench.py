@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Muon step throughput on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: momentum
+update, Frobenius norm, 5 quintic Newton-Schulz iterations and the parameter
+update, for every matrix of the workload, through the C ABI (``muon_step``).
+Inputs (weights, momenta, every step's gradients) are resident in HBM before
+the timed region starts.
+
+Prints ONE JSON line (rank 0): steps/s as ``value``, plus the Newton-Schulz
+TFLOP/s, a roofline entry for the dominant kernel (HIP-event timed launches)
+and the CPU float64 oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+METRIC = "Muon steps/sec + NS TFLOP/s (% bf16 MFMA peak), GPT-2-124M matrix set, 1 GPU"
+DEFAULT_WORKLOAD = "gpt2-124m-hidden"
+
+GEMM_ROLES = ("ns_gram", "ns_poly", "ns_axpy", "ns_axpy_update")
+
+
+def algorithmic_work(wl):
+    """Per-launch algorithmic flops of each Newton-Schulz role and bytes of the
+    momentum pass, summed over the workload's matrices.
+
+    GRAM: m(m+1) n (the m(m+1)/2 distinct entries of X X^T, 2n flops each);
+    POLY: m^2 (m+1) (distinct entries of A A); AXPY: 2 m^2 n.
+    Momentum pass: read g (2 B bf16 / 4 B fp32) and m (4 B), write m' (4 B)
+    and the operand copy of u (2 B bf16 / 4 B fp32).
+    """
+    gb = 2 if wl.storage == "bf16" else 4
+    ub = 2 if wl.compute == "bf16" else 4
+    gram = poly = axpy = 0
+    elems = 0
+    for s in wl.mats:
+        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
+        gram += m * (m + 1) * n
+        poly += m * m * (m + 1)
+        axpy += 2 * m * m * n
+        elems += s.rows * s.cols
+    return {
+        "flops": {"ns_gram": gram, "ns_poly": poly, "ns_axpy": axpy, "ns_axpy_update": axpy},
+        "ns_flops_per_step": wl.ns_steps * (gram + poly + axpy),
+        "momentum_bytes": elems * (gb + 4 + 4 + ub),
+        "elements": elems,
+    }
+
+
+def cpu_baseline(wl, grads_host, budget_s: float):
+    """The oracle, as it stands, on the host cores: whole matrices of the first
+    step until ``budget_s`` seconds of work, extrapolated to one full step."""
+    import oracle
+    from muon_synth import make_momentum, make_param
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    hp = oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
+                      ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c)
+    done_elems, t_used, k = 0, 0.0, 0
+    total = sum(s.rows * s.cols for s in wl.mats)
+    while k < len(wl.mats) and t_used < budget_s:
+        w = oracle.decode(grads_host["param"][k])
+        g = oracle.decode(grads_host["grad0"][k])
+        m = np.asarray(make_momentum(wl, k), dtype=np.float64)
+        t0 = time.perf_counter()
+        oracle.muon_step_matrix(w, g, m, hp)
+        t_used += time.perf_counter() - t0
+        done_elems += wl.mats[k].rows * wl.mats[k].cols
+        k += 1
+    # extrapolate by Newton-Schulz flops (the oracle's cost is its dgemms)
+    from_flops = sum(min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats)
+    done_flops = sum(min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats[:k])
+    est_step_s = t_used * from_flops / max(done_flops, 1)
+    return {
+        "value": 1.0 / est_step_s,
+        "unit": "steps/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{k} of {len(wl.mats)} matrices of step 1 ({done_elems}/{total} elements), "
+                  f"{t_used:.1f} s of float64 NumPy/OpenBLAS, extrapolated to a full step by Newton-Schulz flops",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--grad-sets", type=int, default=0,
+                    help="distinct seeded gradient sets resident in HBM (default: the workload's step count)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
+              "(every matrix's step is independent; the multi-GPU sharding is a design note, not code)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    from muon_synth import encode_storage, make_grad, make_momentum, make_param, workload
+
+    wl = workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = len(wl.mats)
+    n_sets = args.grad_sets or wl.steps
+
+    def upload(stored):
+        if stored.dtype == np.uint16:
+            return torch.from_numpy(stored.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(stored).to(dev)
+
+    t_gen = time.perf_counter()
+    host = {"param": [encode_storage(make_param(wl, i), wl.storage) for i in range(n)]}
+    params = [upload(x) for x in host["param"]]
+    moms = [upload(encode_storage(make_momentum(wl, i), "fp32")) for i in range(n)]
+    grad_sets = []
+    for s in range(1, n_sets + 1):
+        st = [encode_storage(make_grad(wl, s, i), wl.storage) for i in range(n)]
+        if s == 1:
+            host["grad0"] = st
+        grad_sets.append([upload(x) for x in st])
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    hp_c = nsm.Hparams(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
+                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute).to_c()
+    arrays = []
+    for gs in grad_sets:
+        arr = (nsm.muon_matrix * n)()
+        for i in range(n):
+            arr[i] = nsm.make_matrix(params[i], gs[i], moms[i])
+        arrays.append(arr)
+    stream = torch.cuda.current_stream(dev)
+    sptr = int(stream.cuda_stream)
+
+    def run_steps(h, k, start):
+        for j in range(k):
+            st = nsm.muon_step_raw(h, arrays[(start + j) % n_sets], n, hp_c, sptr)
+            if st != 0:
+                raise nsm.MuonError(st, nsm.muon_last_error(h))
+
+    work = algorithmic_work(wl)
+
+    # ---- timed region: plain handle, no per-kernel events ----
+    h = nsm.muon_init(0)
+    run_steps(h, args.warmup, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(h, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ws_bytes = nsm.muon_workspace_bytes(h)
+    nsm.muon_destroy(h)
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- per-kernel HIP-event timing: same steps on a profiling handle ----
+    hp_handle = nsm.muon_init(0, nsm.MUON_INIT_PROFILE)
+    run_steps(hp_handle, args.warmup, 0)
+    torch.cuda.synchronize()
+    nsm.muon_kernel_stats_reset(hp_handle)
+    run_steps(hp_handle, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    stats = nsm.muon_kernel_stats_read(hp_handle)
+    nsm.muon_destroy(hp_handle)
+
+    kernels = {}
+    for name, (launches, total_ms) in stats.items():
+        avg_us = total_ms * 1e3 / max(launches, 1)
+        ent = {"launches": launches, "avg_us": round(avg_us, 2), "ms_per_step": round(total_ms / args.steps, 4)}
+        if name in work["flops"]:
+            ent["tflops"] = round(work["flops"][name] / (avg_us * 1e-6) / 1e12, 2)
+        if name == "momentum_norm":
+            ent["gbs"] = round(work["momentum_bytes"] / (avg_us * 1e-6) / 1e9, 1)
+        kernels[name] = ent
+    ns_ms = sum(stats[r][1] for r in GEMM_ROLES if r in stats) / args.steps
+    ns_tflops = work["ns_flops_per_step"] / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    peak = PEAK_BF16_TFLOPS if wl.compute == "bf16" else PEAK_FP32_TFLOPS
+
+    dom = max((r for r in GEMM_ROLES if r in stats), key=lambda r: stats[r][1])
+    dom_avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
+    achieved = work["flops"][dom] / dom_avg_s / 1e12
+    roofline = {
+        "kernel": f"ns_gemm_kernel ({dom})",
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+    }
+    mom = kernels.get("momentum_norm", {})
+
+    out = {
+        "metric": METRIC,
+        "value": round(args.steps / elapsed, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.compute,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "matrices": n,
+            "elements": work["elements"],
+            "ns_steps": wl.ns_steps,
+            "storage": wl.storage,
+            "grad_sets": n_sets,
+            "nesterov": wl.nesterov,
+            "weight_decay": wl.weight_decay,
+        },
+        "ns_tflops": round(ns_tflops, 2),
+        "ns_frac_peak": round(ns_tflops / peak, 4),
+        "ns_ms_per_step": round(ns_ms, 4),
+        "momentum_hbm_frac": round(mom.get("gbs", 0.0) / PEAK_HBM_GBS, 4) if mom else None,
+        "roofline": roofline,
+        "kernels": kernels,
+        "workspace_gb": round(ws_bytes / 1e9, 3),
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
