@@ -41,6 +41,9 @@ constexpr int kMaxNsSteps = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
+#ifndef MUON_LARGE_TILE_MIN_TILES
+#define MUON_LARGE_TILE_MIN_TILES 512   // large tiles once a phase has this many of them
+#endif
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -55,8 +58,10 @@ struct Plan {
     MatDesc* d_desc = nullptr;
     Tile* d_gram = nullptr;
     int n_gram = 0;
+    int gram_tile = 0;
     Tile* d_axpy = nullptr;
     int n_axpy = 0;
+    int axpy_tile = 0;
     Unit* d_units = nullptr;
     int n_units = 0;
     float* d_partials = nullptr;
@@ -232,13 +237,57 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         for (int64_t r = 0; r < m.R; r += rows_per_unit)
             units.push_back(Unit{i, int32_t(r), int32_t(std::min<int64_t>(m.R, r + rows_per_unit)), 0});
         d.nunits = int32_t(units.size()) - d.unit0;
-        // Newton-Schulz tiles: upper triangle of the m x m products, full m x n grid
-        const int tm = (d.m + kTile - 1) / kTile, tn = (d.n + kTile - 1) / kTile;
-        for (int a = 0; a < tm; ++a)
-            for (int b = a; b < tm; ++b) gram.push_back(Tile{i, a, b, 0});
-        for (int a = 0; a < tm; ++a)
-            for (int b = 0; b < tn; ++b) axpy.push_back(Tile{i, a, b, 0});
         geom[i] = d;
+    }
+
+    // Newton-Schulz tile lists.  One tile edge per phase for the whole call:
+    // the large tile when it still yields a couple of workgroups per CU.
+    auto count_tiles = [&](int T, bool gram) {
+        int64_t c = 0;
+        for (const MatDesc& d : geom) {
+            const int64_t tm = (d.m + T - 1) / T, tn = (d.n + T - 1) / T;
+            c += gram ? tm * (tm + 1) / 2 : tm * tn;
+        }
+        return c;
+    };
+    int gram_tile = kTileF32, axpy_tile = kTileF32;
+    if (!f32c) {
+        gram_tile = count_tiles(kTileLarge, true) >= MUON_LARGE_TILE_MIN_TILES ? kTileLarge : kTileSmall;
+        axpy_tile = count_tiles(kTileLarge, false) >= MUON_LARGE_TILE_MIN_TILES ? kTileLarge : kTileSmall;
+    }
+    // Matrices with the longest k loops first (the hardware dispatches in
+    // order, so the tail holds short tiles); within a matrix, groups of 4 tile
+    // rows sweep the tile columns so concurrent tiles share operand panels.
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    auto build_list = [&](int T, bool gram, std::vector<Tile>& out) {
+        std::vector<int> ord = order;
+        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) {
+            const int64_t kx = gram ? geom[x].n : geom[x].m, ky = gram ? geom[y].n : geom[y].m;
+            return kx > ky;
+        });
+        for (int i : ord) {
+            const MatDesc& d = geom[i];
+            // GRAM/POLY outputs are m x m (upper triangle); AXPY outputs are m x n
+            const int tm = (d.m + T - 1) / T, tn = gram ? tm : (d.n + T - 1) / T;
+            for (int a0 = 0; a0 < tm; a0 += 4)
+                for (int b = 0; b < tn; ++b)
+                    for (int a = a0; a < std::min(tm, a0 + 4); ++a)
+                        if (!gram || b >= a) out.push_back(Tile{i, a, b, 0});
+        }
+    };
+    build_list(gram_tile, true, gram);
+    build_list(axpy_tile, false, axpy);
+    // every tile's operand panels must lie inside the padded workspace buffers
+    for (const Tile& t : gram) {
+        const MatDesc& d = geom[t.mat];
+        if ((t.ti + 1) * gram_tile > d.mp || (t.tj + 1) * gram_tile > d.mp || t.tj < t.ti)
+            return fail(h, MUON_ERR_HIP, "internal: gram tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
+    }
+    for (const Tile& t : axpy) {
+        const MatDesc& d = geom[t.mat];
+        if ((t.ti + 1) * axpy_tile > d.mp || (t.tj + 1) * axpy_tile > d.np)
+            return fail(h, MUON_ERR_HIP, "internal: axpy tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
     }
 
     if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "workspace allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
@@ -280,6 +329,8 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     q.geom = std::move(geom);
     q.n_gram = int(gram.size());
     q.n_axpy = int(axpy.size());
+    q.gram_tile = gram_tile;
+    q.axpy_tile = axpy_tile;
     q.n_units = int(units.size());
     q.key = key;
     q.valid = true;
@@ -394,13 +445,13 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
     }
     for (int it = 1; it <= hp->ns_steps; ++it) {
         pa.iter = it;
-        e = timed(h, K_GRAM, stream, [&] { return launch_ns_phase(PH_GRAM, f32c, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        e = timed(h, K_GRAM, stream, [&] { return launch_ns_phase(PH_GRAM, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
         if (e != hipSuccess) return hip_fail(h, e, "gram launch");
-        e = timed(h, K_POLY, stream, [&] { return launch_ns_phase(PH_POLY, f32c, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        e = timed(h, K_POLY, stream, [&] { return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
         if (e != hipSuccess) return hip_fail(h, e, "poly launch");
         const bool last = it == hp->ns_steps;
         e = timed(h, last ? K_AXPY_LAST : K_AXPY, stream, [&] {
-            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.d_axpy, plan.n_axpy, plan.d_desc, pa, stream);
+            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.axpy_tile, plan.d_axpy, plan.n_axpy, plan.d_desc, pa, stream);
         });
         if (e != hipSuccess) return hip_fail(h, e, "axpy launch");
     }

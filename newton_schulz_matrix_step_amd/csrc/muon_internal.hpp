@@ -72,12 +72,15 @@ hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, 
                            bool f32_compute, hipStream_t s);
 hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials,
                                 float* inv_norm, float* nu, float eps, hipStream_t s);
-hipError_t launch_ns_phase(int kind, bool f32_compute, const Tile* tiles, int n_tiles,
+hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* tiles, int n_tiles,
                            const MatDesc* mats, PhaseArgs a, hipStream_t s);
 hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats,
                                 PhaseArgs a, hipStream_t s);
 
-// Tile edge used by the Newton-Schulz GEMMs.
-constexpr int kTile = 128;
+// Tile edges of the Newton-Schulz GEMMs: fp32 mode uses kTileF32; bf16 mode
+// picks kTileLarge or kTileSmall per phase from the tile count.
+constexpr int kTileF32 = 128;
+constexpr int kTileLarge = 256;
+constexpr int kTileSmall = 128;
 
 }  // namespace muon

@@ -222,7 +222,7 @@ __device__ __forceinline__ int swz(int r, int ch) { return ch ^ ((r ^ (r >> 3)) 
 
 template <bool F32>
 struct GemmCfg {
-    static constexpr int BM = kTile;               // square output tiles
+    static constexpr int BM = kTileF32;            // square output tiles
     static constexpr int EPC = F32 ? 4 : 8;        // elements per 16-byte chunk
     static constexpr int ES = F32 ? 4 : 2;         // element bytes
     static constexpr int BK = EPC * 8;             // k per block: 8 chunks per LDS row
@@ -307,124 +307,69 @@ __device__ __forceinline__ void sstore(u32x4_t* __restrict__ s, bool kc, const u
     }
 }
 
-template <int KIND, bool F32>
-__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restrict__ tiles,
-                                                           const MatDesc* __restrict__ mats, PhaseArgs pa) {
-    using G = GemmCfg<F32>;
-    constexpr int BM = G::BM, BK = G::BK, TI = G::TI, WM = G::WM;
-    __shared__ u32x4_t sA[2][BM * 8];
-    __shared__ u32x4_t sB[2][BM * 8];
-
-    const Tile t = tiles[blockIdx.x];
-    const MatDesc& md = mats[t.mat];
-    char* const ws = pa.ws;
-    const int it = pa.iter;
-
-    // current X: the momentum pass's copy of u (stored orientation) on the first
-    // iteration, afterwards the operand copy written by the previous iteration
-    const int64_t off_cur = (it == 1) ? md.off_u : (((it - 2) & 1) ? md.off_xb1 : md.off_xb0);
-    const char* pa_ptr;
-    const char* pb_ptr;
+// Operands of one Newton-Schulz product for one matrix.  "kc": element (row, k)
+// at ptr[row * ld + k]; otherwise at ptr[k * ld + row].
+struct Operands {
+    const char* a;
+    const char* b;
     int64_t lda, ldb;
     bool a_kc, b_kc;
     int K;
+    int64_t off_cur;   // workspace offset of the current X operand copy
+};
+
+template <int KIND>
+__device__ __forceinline__ Operands resolve_operands(const MatDesc& md, const PhaseArgs& pa) {
+    Operands o;
+    const char* ws = pa.ws;
+    const int it = pa.iter;
+    // current X: the momentum pass's copy of u (stored orientation) on the first
+    // iteration, afterwards the operand copy written by the previous iteration
+    o.off_cur = (it == 1) ? md.off_u : (((it - 2) & 1) ? md.off_xb1 : md.off_xb0);
     if (KIND == PH_GRAM) {
-        K = md.n;
-        pa_ptr = pb_ptr = ws + off_cur;
+        // A = X X^T: both operands are rows of X
+        o.K = md.n;
+        o.a = o.b = ws + o.off_cur;
         if (it == 1) {
-            lda = ldb = md.Cp;
-            a_kc = b_kc = !md.trans;
+            o.lda = o.ldb = md.Cp;
+            o.a_kc = o.b_kc = !md.trans;   // X0 = U^T when transposed
         } else {
-            lda = ldb = md.np;
-            a_kc = b_kc = true;
+            o.lda = o.ldb = md.np;
+            o.a_kc = o.b_kc = true;
         }
     } else if (KIND == PH_POLY) {
-        K = md.m;
-        pa_ptr = pb_ptr = ws + md.off_a;
-        lda = ldb = md.mp;
-        a_kc = b_kc = true;
+        // A A = A A^T (A symmetric): both operands are rows of A
+        o.K = md.m;
+        o.a = o.b = ws + md.off_a;
+        o.lda = o.ldb = md.mp;
+        o.a_kc = o.b_kc = true;
     } else {
-        K = md.m;
-        pa_ptr = ws + md.off_b;
-        lda = md.mp;
-        a_kc = true;
-        pb_ptr = ws + off_cur;
+        // B X: rows of B, columns of X (X^T rows when X0 = U^T)
+        o.K = md.m;
+        o.a = ws + md.off_b;
+        o.lda = md.mp;
+        o.a_kc = true;
+        o.b = ws + o.off_cur;
         if (it == 1) {
-            ldb = md.Cp;
-            b_kc = md.trans != 0;
+            o.ldb = md.Cp;
+            o.b_kc = md.trans != 0;
         } else {
-            ldb = md.np;
-            b_kc = false;
+            o.ldb = md.np;
+            o.b_kc = false;
         }
     }
+    return o;
+}
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wr = (wave >> 1) * WM, wc = (wave & 1) * WM;
-    const int row_a0 = t.ti * BM, row_b0 = t.tj * BM;
-
-    f32x4_t acc[TI][TI];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    u32x4_t ra[G::NREG], rb[G::NREG];
-    const int nk = (K + BK - 1) / BK;
-    gload<F32>(pa_ptr, lda, a_kc, row_a0, 0, ra);
-    gload<F32>(pb_ptr, ldb, b_kc, row_b0, 0, rb);
-    sstore<F32>(sA[0], a_kc, ra);
-    sstore<F32>(sB[0], b_kc, rb);
-    __syncthreads();
-
-    for (int kb = 0; kb < nk; ++kb) {
-        const int cur = kb & 1;
-        const bool more = kb + 1 < nk;
-        if (more) {
-            gload<F32>(pa_ptr, lda, a_kc, row_a0, (kb + 1) * BK, ra);
-            gload<F32>(pb_ptr, ldb, b_kc, row_b0, (kb + 1) * BK, rb);
-        }
-        const u32x4_t* __restrict__ cA = sA[cur];
-        const u32x4_t* __restrict__ cB = sB[cur];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int ch = 4 * s + (lane >> 4);
-            u32x4_t fa[TI], fb[TI];
-#pragma unroll
-            for (int i = 0; i < TI; ++i) {
-                const int r = wr + 16 * i + (lane & 15);
-                fa[i] = cA[r * 8 + swz(r, ch)];
-                const int c = wc + 16 * i + (lane & 15);
-                fb[i] = cB[c * 8 + swz(c, ch)];
-            }
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int j = 0; j < TI; ++j) {
-                    if (F32) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(fa[i][e]),
-                                                                             __uint_as_float(fb[j][e]), acc[i][j], 0, 0, 0);
-                    } else {
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
-                                                                            __builtin_bit_cast(bf16x8_t, fb[j]),
-                                                                            acc[i][j], 0, 0, 0);
-                    }
-                }
-        }
-        if (more) {
-            sstore<F32>(sA[cur ^ 1], a_kc, ra);
-            sstore<F32>(sB[cur ^ 1], b_kc, rb);
-        }
-        __syncthreads();
-    }
-
-    // Epilogue.  MFMA 16x16 output layout: lane holds column (lane & 15) and
-    // rows 4 * (lane >> 4) + e, e = 0..3, of each 16 x 16 tile.
-    const int gr0 = row_a0 + wr + 4 * (lane >> 4);
-    const int gc0 = row_b0 + wc + (lane & 15);
+// Epilogue of one output tile.  acc[i][j][e] is element
+// (gr0 + 16 i + e, gc0 + 16 j) of the NS-orientation product (MFMA 16x16
+// output layout: lane holds column lane & 15 and rows 4 (lane >> 4) + e).
+template <int KIND, bool F32, int TI>
+__device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                         const f32x4_t (&acc)[TI][TI], int gr0, int gc0, int64_t off_cur) {
+    char* const ws = pa.ws;
+    const int it = pa.iter;
     constexpr int ODT = F32 ? 1 : 0;  // workspace element type
-
     if (KIND == PH_GRAM || KIND == PH_POLY) {
         const int m = md.m;
         const int64_t ld = md.mp;
@@ -443,6 +388,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = gr0 + 16 * i + e, c = gc0 + 16 * j;
+                    // upper triangle (r <= c on diagonal tiles) written twice: (r, c) and (c, r)
                     if (r < m && c < m && (!diag || r <= c)) {
                         float v = acc[i][j][e];
                         if (KIND == PH_GRAM)
@@ -489,6 +435,220 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
                     }
                 }
     }
+}
+
+// Workgroups are handed to the 8 XCDs round-robin; give each XCD a contiguous
+// range of the tile list so neighbouring tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int bid, int n) {
+    const int q = n >> 3, r = n & 7;
+    const int x = bid & 7, idx = bid >> 3;
+    return (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 validation-mode GEMM: 128 x 128 tiles, register-staged loads
+// ---------------------------------------------------------------------------
+template <int KIND, bool F32>
+__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restrict__ tiles,
+                                                           const MatDesc* __restrict__ mats, PhaseArgs pa) {
+    using G = GemmCfg<F32>;
+    constexpr int BM = G::BM, BK = G::BK, TI = G::TI, WM = G::WM;
+    __shared__ u32x4_t sA[2][BM * 8];
+    __shared__ u32x4_t sB[2][BM * 8];
+
+    const Tile t = tiles[blockIdx.x];
+    const MatDesc& md = mats[t.mat];
+    const Operands op = resolve_operands<KIND>(md, pa);
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wr = (wave >> 1) * WM, wc = (wave & 1) * WM;
+    const int row_a0 = t.ti * BM, row_b0 = t.tj * BM;
+
+    f32x4_t acc[TI][TI];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t ra[G::NREG], rb[G::NREG];
+    const int nk = (op.K + BK - 1) / BK;
+    gload<F32>(op.a, op.lda, op.a_kc, row_a0, 0, ra);
+    gload<F32>(op.b, op.ldb, op.b_kc, row_b0, 0, rb);
+    sstore<F32>(sA[0], op.a_kc, ra);
+    sstore<F32>(sB[0], op.b_kc, rb);
+    __syncthreads();
+
+    for (int kb = 0; kb < nk; ++kb) {
+        const int cur = kb & 1;
+        const bool more = kb + 1 < nk;
+        if (more) {
+            gload<F32>(op.a, op.lda, op.a_kc, row_a0, (kb + 1) * BK, ra);
+            gload<F32>(op.b, op.ldb, op.b_kc, row_b0, (kb + 1) * BK, rb);
+        }
+        const u32x4_t* __restrict__ cA = sA[cur];
+        const u32x4_t* __restrict__ cB = sB[cur];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ch = 4 * s + (lane >> 4);
+            u32x4_t fa[TI], fb[TI];
+#pragma unroll
+            for (int i = 0; i < TI; ++i) {
+                const int r = wr + 16 * i + (lane & 15);
+                fa[i] = cA[r * 8 + swz(r, ch)];
+                const int c = wc + 16 * i + (lane & 15);
+                fb[i] = cB[c * 8 + swz(c, ch)];
+            }
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TI; ++j) {
+                    if (F32) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(fa[i][e]),
+                                                                             __uint_as_float(fb[j][e]), acc[i][j], 0, 0, 0);
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fa[i]),
+                                                                            __builtin_bit_cast(bf16x8_t, fb[j]),
+                                                                            acc[i][j], 0, 0, 0);
+                    }
+                }
+        }
+        if (more) {
+            sstore<F32>(sA[cur ^ 1], op.a_kc, ra);
+            sstore<F32>(sB[cur ^ 1], op.b_kc, rb);
+        }
+        __syncthreads();
+    }
+    epilogue<KIND, F32, TI>(md, t, pa, acc, row_a0 + wr + 4 * (lane >> 4), row_b0 + wc + (lane & 15), op.off_cur);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 GEMM: BM x BM tiles (BM = 256 or 128), 4 waves of (BM/2)^2, BK = 64.
+//
+// Global -> LDS with direct-to-LDS 16-byte loads (no staging registers), two
+// LDS stages, one barrier per k-block.  Row-contiguous operands sit in LDS as
+// [row][8 chunks of 8 k] (chunk XOR-swizzled by row & 7) and feed the MFMA with
+// ds_read_b128; k-strided operands sit as [k][BM] (chunk XOR-swizzled by
+// 2 (k & 7)) and feed it with ds_read_b64_tr_b16, which hands lane j of each
+// 16-lane group column j of a 4 x 16 block.
+// ---------------------------------------------------------------------------
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+#ifndef LDS_AS
+#define LDS_AS __attribute__((address_space(3)))
+#endif
+
+template <int BM>
+struct BfCfg {
+    static constexpr int BK = 64;
+    static constexpr int WT = BM / 2;             // wave tile edge
+    static constexpr int TI = WT / 16;            // MFMA tiles per wave edge
+    static constexpr int OPB = BM * BK * 2;       // LDS bytes of one operand stage
+    static constexpr int LPW = OPB / 1024 / 4;    // 1 KB direct loads per wave per operand
+    static constexpr int CPR = BM / 8;            // 16-byte chunks per [k][BM] row
+    static constexpr int RPK = 64 / CPR;          // [k][BM] rows per 1 KB
+};
+
+__device__ __forceinline__ int kswz(int k) { return (2 * k) & 14; }
+
+// Issue the direct-to-LDS loads of one operand stage.
+template <int BM>
+__device__ __forceinline__ void lds_fill(char* __restrict__ lds, const char* __restrict__ g, int64_t ld, bool kc,
+                                         int row0, int k0, int wave, int lane) {
+    using C = BfCfg<BM>;
+#pragma unroll
+    for (int q = 0; q < C::LPW; ++q) {
+        const int blk = wave * C::LPW + q;
+        const char* src;
+        if (kc) {
+            const int r = blk * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);
+            src = g + (int64_t(row0 + r) * ld + k0 + c * 8) * 2;
+        } else {
+            const int k = blk * C::RPK + lane / C::CPR;
+            const int c = (lane % C::CPR) ^ kswz(k);
+            src = g + (int64_t(k0 + k) * ld + row0 + c * 8) * 2;
+        }
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(lds + blk * 1024), 16, 0, 0);
+    }
+}
+
+// One MFMA operand fragment: 8 k values (k = 32 s + 8 (lane >> 4) + e) of
+// row/column `rc` of the stage.
+template <int BM>
+__device__ __forceinline__ bf16x8_t frag(const char* __restrict__ lds, bool kc, int rc16, int s, int lane) {
+    if (kc) {
+        const int r = rc16 + (lane & 15);
+        const int c = (4 * s + (lane >> 4)) ^ (r & 7);
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lds + r * 128 + c * 16));
+    }
+    const int i = lane & 15;
+    const int n = rc16 + 4 * (i & 3);
+    i16x4_t h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int k = 32 * s + 8 * (lane >> 4) + 4 * hh + (i >> 2);
+        const int c = (n >> 3) ^ kswz(k);
+        const char* p = lds + k * (BM * 2) + c * 16 + (n & 7) * 2;
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(p));
+    }
+    const i16x4_t lo = h[0], hi = h[1];
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int KIND, int BM>
+__global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
+                                                            const MatDesc* __restrict__ mats, PhaseArgs pa,
+                                                            int n_tiles) {
+    using C = BfCfg<BM>;
+    constexpr int TI = C::TI, WT = C::WT;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * C::OPB];   // [stage][A | B]
+
+    const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
+    const MatDesc& md = mats[t.mat];
+    const Operands op = resolve_operands<KIND>(md, pa);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wr = (wave >> 1) * WT, wc = (wave & 1) * WT;
+    const int row_a0 = t.ti * BM, row_b0 = t.tj * BM;
+
+    f32x4_t acc[TI][TI];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (op.K + C::BK - 1) / C::BK;
+    lds_fill<BM>(smem, op.a, op.lda, op.a_kc, row_a0, 0, wave, lane);
+    lds_fill<BM>(smem + C::OPB, op.b, op.ldb, op.b_kc, row_b0, 0, wave, lane);
+
+    for (int kb = 0; kb < nk; ++kb) {
+        char* cur = smem + (kb & 1) * 2 * C::OPB;
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage kb have landed
+        __syncthreads();                 // ... and every wave's; stage kb-1 is free
+        if (kb + 1 < nk) {
+            char* nxt = smem + ((kb + 1) & 1) * 2 * C::OPB;
+            lds_fill<BM>(nxt, op.a, op.lda, op.a_kc, row_a0, (kb + 1) * C::BK, wave, lane);
+            lds_fill<BM>(nxt + C::OPB, op.b, op.ldb, op.b_kc, row_b0, (kb + 1) * C::BK, wave, lane);
+        }
+        const char* sa = cur;
+        const char* sb = cur + C::OPB;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8_t fa[TI], fb[TI];
+#pragma unroll
+            for (int i = 0; i < TI; ++i) fa[i] = frag<BM>(sa, op.a_kc, wr + 16 * i, s, lane);
+#pragma unroll
+            for (int j = 0; j < TI; ++j) fb[j] = frag<BM>(sb, op.b_kc, wc + 16 * j, s, lane);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    epilogue<KIND, false, TI>(md, t, pa, acc, row_a0 + wr + 4 * (lane >> 4), row_b0 + wc + (lane & 15), op.off_cur);
 }
 
 // ---------------------------------------------------------------------------
@@ -549,21 +709,25 @@ hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* pa
 }
 
 template <int KIND>
-static void launch_kind(bool f32c, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s) {
+static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
+                        hipStream_t s) {
     if (f32c)
         hipLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a);
+    else if (tile == 256)
+        hipLaunchKernelGGL((ns_gemm_bf16<KIND, 256>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
     else
-        hipLaunchKernelGGL((ns_gemm_kernel<KIND, false>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a);
+        hipLaunchKernelGGL((ns_gemm_bf16<KIND, 128>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
 }
 
-hipError_t launch_ns_phase(int kind, bool f32c, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
-                           hipStream_t s) {
+hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
+                           PhaseArgs a, hipStream_t s) {
     if (n_tiles <= 0) return hipSuccess;
+    if (f32c ? tile != 128 : (tile != 128 && tile != 256)) return hipErrorInvalidValue;
     switch (kind) {
-        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tiles, n_tiles, mats, a, s); break;
-        case PH_POLY: launch_kind<PH_POLY>(f32c, tiles, n_tiles, mats, a, s); break;
-        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tiles, n_tiles, mats, a, s); break;
-        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tiles, n_tiles, mats, a, s); break;
+        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s); break;
+        case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s); break;
+        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tile, tiles, n_tiles, mats, a, s); break;
+        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tile, tiles, n_tiles, mats, a, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
