@@ -397,6 +397,14 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
         d.ld_upd = m.ld_upd;
         d.vec_ok = (m.C % 8 == 0) && (m.ld_grad % 8 == 0) && aligned16(m.grad) &&
                    (!m.has_mom || ((m.ld_mom % 8 == 0) && aligned16(m.mom)));
+        {
+            const int64_t pe = m.dtype == MUON_BF16 ? 8 : 16;   // bytes of 4 param/grad elements
+            auto al = [](const void* q, int64_t b) { return (reinterpret_cast<uintptr_t>(q) % uintptr_t(b)) == 0; };
+            d.vec_io = (m.C % 4 == 0) && (m.ld_grad % 4 == 0) && al(m.grad, pe) &&
+                       (!m.has_param || ((m.ld_param % 4 == 0) && al(m.param, pe))) &&
+                       (!m.has_mom || ((m.ld_mom % 4 == 0) && al(m.mom, 16))) &&
+                       (!m.upd || ((m.ld_upd % 4 == 0) && al(m.upd, 16)));
+        }
     }
     hipError_t e;
     if (!plan.have_uploaded || std::memcmp(desc.data(), plan.uploaded.data(), sizeof(MatDesc) * n) != 0) {

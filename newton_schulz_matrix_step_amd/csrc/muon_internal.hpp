@@ -25,8 +25,10 @@ struct MatDesc {
     int32_t has_param;         // 0 for the orthogonalise-only entry point
     int32_t has_mom;           // 0: u = g (no momentum buffer)
     int32_t unit0, nunits;     // momentum-pass units owned by this matrix
-    int32_t vec_ok;            // 16-byte vector path legal for param/grad/mom/upd
+    int32_t vec_ok;            // momentum pass: 8-element vectors legal for grad/mom
+    int32_t vec_io;            // epilogues: 4-element vectors legal for param/grad/mom/upd
     float shape_scale;         // sqrt(max(1, R / C))
+    int32_t pad0;
     int64_t off_u;             // workspace byte offsets
     int64_t off_xm;            // fp32 master X (bf16 mode only)
     int64_t off_xb0, off_xb1;  // operand copies of X, ping-pong

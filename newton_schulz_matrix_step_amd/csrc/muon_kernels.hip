@@ -596,6 +596,228 @@ __device__ __forceinline__ bf16x8_t frag(const char* __restrict__ lds, bool kc, 
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t ld4_bf16(const void* p) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+    return f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                   __uint_as_float(w[1] & 0xFFFF0000u)};
+}
+__device__ __forceinline__ void st4_bf16(void* p, f32x4_t v) {
+    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+// 4 consecutive elements of a caller buffer (dtype 0 bf16 / 1 f32); `vec`: aligned and in range
+__device__ __forceinline__ f32x4_t ld4_io(const void* p, int64_t i, int dt, bool vec, int nvalid) {
+    if (vec) {
+        if (dt == 0) return ld4_bf16(static_cast<const uint16_t*>(p) + i);
+        return *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+    }
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < nvalid) v[q] = load_elem(p, i + q, dt);
+    return v;
+}
+__device__ __forceinline__ void st4_io(void* p, int64_t i, int dt, bool vec, int nvalid, f32x4_t v) {
+    if (vec) {
+        if (dt == 0)
+            st4_bf16(static_cast<uint16_t*>(p) + i, v);
+        else
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i) = v;
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < nvalid) store_elem(p, i + q, dt, v[q]);
+}
+
+// u at 4 consecutive stored elements (r, c..c+3)
+__device__ __forceinline__ f32x4_t u4_at(const MatDesc& md, int64_t r, int64_t c, float beta, bool nest, bool vec,
+                                         int nvalid) {
+    const f32x4_t g = ld4_io(md.grad, r * md.ld_grad + c, md.io_dtype, vec, nvalid);
+    if (!md.has_mom) return g;
+    const f32x4_t mn = ld4_io(md.mom, r * md.ld_mom + c, 1, vec, nvalid);
+    if (!nest) return mn;
+    f32x4_t u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) u[q] = fmaf(beta, mn[q], g[q]);
+    return u;
+}
+
+// Epilogue through LDS.  Each wave stages its (16 x WT) row bands in fp32 in its
+// own LDS region and reads them back as 4-element runs along rows (row-major
+// pass) or down columns (column-major pass), so global traffic moves in 8- and
+// 16-byte vectors along contiguous rows of the destination.
+template <int KIND, int TI>
+__device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                                const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                                float* __restrict__ stg) {
+    constexpr int WT = TI * 16, LDW = WT + 4;
+    char* const ws = pa.ws;
+    const int it = pa.iter;
+    const int m = md.m, n = md.n;
+    const bool trans = md.trans != 0;
+    const bool nest = pa.nesterov != 0;
+    const bool vio = md.vec_io != 0;
+    const bool gp = (KIND == PH_GRAM || KIND == PH_POLY);
+    const bool diag = gp && t.ti == t.tj;
+    // GRAM/POLY: out (and A for POLY); AXPY: X master / operand copies
+    const int64_t ldq = gp ? md.mp : md.np;
+    uint16_t* out = reinterpret_cast<uint16_t*>(ws + (KIND == PH_GRAM ? md.off_a : md.off_b));
+    const uint16_t* ain = reinterpret_cast<const uint16_t*>(ws + md.off_a);
+    float scl = 1.f;
+    if (KIND == PH_GRAM && it == 1) {
+        const float s = pa.inv_norm[t.mat];
+        scl = s * s;
+    }
+    const float alpha = (it == 1) ? pa.inv_norm[t.mat] : 1.f;
+    float* xm = reinterpret_cast<float*>(ws + md.off_xm);
+    uint16_t* xb_next = reinterpret_cast<uint16_t*>(ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
+    const float wdec = 1.f - pa.lr * pa.wd;
+    const float step = pa.lr * md.shape_scale;
+    const bool row_pass = gp || KIND == PH_AXPY || !trans;
+    const bool col_pass = gp || (KIND == PH_AXPY_LAST && trans);
+    const int g = lane >> 4, c16 = lane & 15;
+
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+        for (int j = 0; j < TI; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) stg[(4 * g + e) * LDW + 16 * j + c16] = acc[i][j][e];
+        const int rb = row0 + 16 * i;
+        if (row_pass) {
+#pragma unroll 2
+            for (int q = 0; q < WT / 16; ++q) {
+                const int idx = q * 256 + lane * 4;
+                const int lr = idx / WT, lc = idx % WT;
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * LDW + lc);
+                const int r = rb + lr, c = col0 + lc;
+                if (gp) {
+                    if (r >= m) continue;
+                    int nv = m - c;                 // columns inside the matrix
+                    nv = nv > 4 ? 4 : nv;
+                    int first = 0;                  // diagonal tiles keep r <= c
+                    if (diag && r > c) first = r - c;
+                    if (nv <= first) continue;
+                    const int64_t o = int64_t(r) * ldq + c;
+                    f32x4_t w;
+                    if (KIND == PH_GRAM) {
+                        w = v * scl;
+                    } else {
+                        const f32x4_t a4 = (nv == 4) ? ld4_bf16(ain + o) : ld4_io(ain, o, 0, false, nv);
+                        w = pa.b * a4 + pa.c * v;
+                    }
+                    if (nv == 4 && first == 0)
+                        st4_bf16(out + o, w);
+                    else
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2)
+                            if (q2 >= first && q2 < nv) out[o + q2] = f32_to_bf16(w[q2]);
+                } else {
+                    if (r >= m || c >= n) continue;
+                    int nv = n - c;
+                    nv = nv > 4 ? 4 : nv;
+                    f32x4_t master;
+                    if (it == 1)
+                        master = trans ? f32x4_t{u_at(md, c, r, pa.beta, nest),
+                                                 nv > 1 ? u_at(md, c + 1, r, pa.beta, nest) : 0.f,
+                                                 nv > 2 ? u_at(md, c + 2, r, pa.beta, nest) : 0.f,
+                                                 nv > 3 ? u_at(md, c + 3, r, pa.beta, nest) : 0.f}
+                                       : u4_at(md, r, c, pa.beta, nest, vio && nv == 4, nv);
+                    else
+                        master = *reinterpret_cast<const f32x4_t*>(xm + int64_t(r) * ldq + c);  // padded: in bounds
+                    f32x4_t x = alpha * (pa.a * master + v);
+                    if (KIND == PH_AXPY) {
+                        const int64_t o = int64_t(r) * ldq + c;
+                        if (nv == 4) {
+                            *reinterpret_cast<f32x4_t*>(xm + o) = x;
+                            st4_bf16(xb_next + o, x);
+                        } else {
+#pragma unroll
+                            for (int q2 = 0; q2 < 4; ++q2)
+                                if (q2 < nv) {
+                                    xm[o + q2] = x[q2];
+                                    xb_next[o + q2] = f32_to_bf16(x[q2]);
+                                }
+                        }
+                    } else {  // last iteration, stored orientation = NS orientation
+                        const bool vec = vio && nv == 4;
+                        if (md.has_param) {
+                            const int64_t pi = int64_t(r) * md.ld_param + c;
+                            const f32x4_t w = ld4_io(md.param, pi, md.io_dtype, vec, nv);
+                            f32x4_t wn;
+#pragma unroll
+                            for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-step, x[q2], w[q2] * wdec);
+                            st4_io(md.param, pi, md.io_dtype, vec, nv, wn);
+                        }
+                        if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, x);
+                    }
+                }
+            }
+        }
+        if (col_pass) {
+#pragma unroll 2
+            for (int q = 0; q < WT / 16; ++q) {
+                const int task = q * 64 + lane;
+                const int lc = task % WT, quad = task / WT;
+                const int r = rb + 4 * quad, c = col0 + lc;   // elements (r..r+3, c)
+                f32x4_t v;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(4 * quad + q2) * LDW + lc];
+                if (gp) {
+                    // mirror: (r + q2, c) -> (c, r + q2); diagonal tiles mirror only r + q2 < c
+                    if (c >= m) continue;
+                    int nv = m - r;
+                    nv = nv > 4 ? 4 : nv;
+                    if (diag) {
+                        const int lim = c - r;        // q2 < lim  <=>  r + q2 < c
+                        nv = nv < lim ? nv : lim;
+                    }
+                    if (nv <= 0) continue;
+                    const int64_t o = int64_t(c) * ldq + r;
+                    f32x4_t w;
+                    if (KIND == PH_GRAM) {
+                        w = v * scl;
+                    } else {
+                        const f32x4_t a4 = (nv == 4) ? ld4_bf16(ain + o) : ld4_io(ain, o, 0, false, nv);  // A symmetric
+                        w = pa.b * a4 + pa.c * v;
+                    }
+                    if (nv == 4)
+                        st4_bf16(out + o, w);
+                    else
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2)
+                            if (q2 < nv) out[o + q2] = f32_to_bf16(w[q2]);
+                } else {
+                    // last iteration of a transposed matrix: NS (r + q2, c) is stored (c, r + q2)
+                    if (c >= n || r >= m) continue;
+                    int nv = m - r;
+                    nv = nv > 4 ? 4 : nv;
+                    const bool vec = vio && nv == 4;
+                    f32x4_t master;
+                    if (it == 1) {
+                        master = u4_at(md, c, r, pa.beta, nest, vec, nv);
+                    } else {
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2) master[q2] = xm[int64_t(r + q2) * ldq + c];  // padded rows
+                    }
+                    const f32x4_t x = alpha * (pa.a * master + v);
+                    if (md.has_param) {
+                        const int64_t pi = int64_t(c) * md.ld_param + r;
+                        const f32x4_t w = ld4_io(md.param, pi, md.io_dtype, vec, nv);
+                        f32x4_t wn;
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-step, x[q2], w[q2] * wdec);
+                        st4_io(md.param, pi, md.io_dtype, vec, nv, wn);
+                    }
+                    if (md.upd) st4_io(md.upd, int64_t(c) * md.ld_upd + r, 1, vec, nv, x);
+                }
+            }
+        }
+    }
+}
+
 template <int KIND, int BM>
 __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
                                                             const MatDesc* __restrict__ mats, PhaseArgs pa,
@@ -648,7 +870,9 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
     }
-    epilogue<KIND, false, TI>(md, t, pa, acc, row_a0 + wr + 4 * (lane >> 4), row_b0 + wc + (lane & 15), op.off_cur);
+    __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+    epilogue_staged<KIND, TI>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
+                              reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
 }
 
 // ---------------------------------------------------------------------------
