@@ -20,6 +20,8 @@
 // as [row][k] in 16-byte chunks, XOR-swizzled; an operand whose k index is the
 // row index in memory is transposed in registers on its way to LDS.
 
+#include <type_traits>
+
 #include "muon_internal.hpp"
 
 namespace muon {
@@ -524,63 +526,105 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
 }
 
 // ---------------------------------------------------------------------------
-// bf16 GEMM: BM x BM tiles (BM = 256 or 128), 4 waves of (BM/2)^2, BK = 64.
+// bf16 GEMM: BM x BM tiles (BM = 256 or 128), 4 waves of (BM/2)^2 outputs each,
+// k blocks of 32 through a ring of 4 LDS stages, loads issued 3 blocks ahead.
 //
-// Global -> LDS with direct-to-LDS 16-byte loads (no staging registers), two
-// LDS stages, one barrier per k-block.  Row-contiguous operands sit in LDS as
-// [row][8 chunks of 8 k] (chunk XOR-swizzled by row & 7) and feed the MFMA with
-// ds_read_b128; k-strided operands sit as [k][BM] (chunk XOR-swizzled by
-// 2 (k & 7)) and feed it with ds_read_b64_tr_b16, which hands lane j of each
-// 16-lane group column j of a 4 x 16 block.
+// Global -> LDS uses direct-to-LDS 16-byte loads (no staging registers),
+// issued from inline asm with explicit vmcnt waits: every stage is waited for
+// exactly when it is consumed, so three blocks of loads stay in flight behind
+// the MFMAs.  Row-contiguous operands sit in LDS as [row][4 chunks of 8 k]
+// (chunk XOR (row >> 1) & 3) and feed the MFMA with ds_read_b128; k-strided
+// operands sit as [k][BM] (chunk XOR 2 (k & 7)) and feed it with
+// ds_read_b64_tr_b16, which hands lane j of each 16-lane group column j of a
+// 4 x 16 block.  Operand layouts are template parameters so the k loop is
+// straight-line code.
 // ---------------------------------------------------------------------------
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #ifndef LDS_AS
 #define LDS_AS __attribute__((address_space(3)))
 #endif
 
-template <int BM>
+template <int BM, int BK_ = 64>
 struct BfCfg {
-    static constexpr int BK = 64;
+    static constexpr int BK = BK_;                // k per LDS stage (32 or 64)
+    static constexpr int NST = BK == 64 ? 2 : 4;  // LDS stages (ring)
+    static constexpr int CPK = BK / 8;            // 16-byte chunks per [row][BK] row
     static constexpr int WT = BM / 2;             // wave tile edge
     static constexpr int TI = WT / 16;            // MFMA tiles per wave edge
     static constexpr int OPB = BM * BK * 2;       // LDS bytes of one operand stage
-    static constexpr int LPW = OPB / 1024 / 4;    // 1 KB direct loads per wave per operand
+    static constexpr int STB = 2 * OPB;           // LDS bytes of one stage (A then B)
+    static constexpr int LPW = OPB / 1024 / 4;    // 1 KB loads per wave per operand per stage
+    static constexpr int LPS = 2 * LPW;           // loads per wave per stage
     static constexpr int CPR = BM / 8;            // 16-byte chunks per [k][BM] row
     static constexpr int RPK = 64 / CPR;          // [k][BM] rows per 1 KB
 };
+constexpr int kBK = 64;
 
-__device__ __forceinline__ int kswz(int k) { return (2 * k) & 14; }
+// Swizzle of the 16-byte chunks of a [k][BM] LDS row.  A ds_read_b64_tr_b16
+// group of 16 lanes reads rows k0..k0+3 (4 rows x 32 bytes): bits 1-2 spread
+// those rows over one 128-byte window; bit 3 puts the neighbouring 16-lane
+// group (rows 8 further on) in the other 128-byte half of the bank space.
+__device__ __forceinline__ int kswz(int k) { return ((2 * k) & 6) | ((((k >> 3) ^ (k >> 2)) & 1) << 3); }
 
-// Issue the direct-to-LDS loads of one operand stage.
-template <int BM>
-__device__ __forceinline__ void lds_fill(char* __restrict__ lds, const char* __restrict__ g, int64_t ld, bool kc,
-                                         int row0, int k0, int wave, int lane) {
-    using C = BfCfg<BM>;
+// Swizzle of the 16-byte chunks of a [row][CPK chunks] LDS row: the 8 rows a
+// ds_read_b128 phase touches land on 8 distinct 16-byte bank groups.
+template <int CPK>
+__device__ __forceinline__ int kcswz(int r) { return CPK == 8 ? (r & 7) : ((r >> 1) & 3); }
+
+#ifndef MUON_LDS_DMA16
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
+// at lds + 16 L (lds must be wave-uniform).  Nothing is returned in registers;
+// completion is tracked by vmcnt and waited for with vm_wait().
+__device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+#else
+#define lds_dma16 MUON_LDS_DMA16
+#endif
+
+// s_waitcnt vmcnt(N), no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Issue the loads of one operand of one stage.
+template <int BM, int BK, bool KC>
+__device__ __forceinline__ void issue_operand(char* __restrict__ lds, const char* __restrict__ g, int64_t ld, int row0,
+                                              int k0, int wave, int lane) {
+    using C = BfCfg<BM, BK>;
 #pragma unroll
     for (int q = 0; q < C::LPW; ++q) {
         const int blk = wave * C::LPW + q;
         const char* src;
-        if (kc) {
-            const int r = blk * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ (r & 7);
+        if (KC) {
+            // [row][CPK chunks]: 64 / CPK rows per 1 KB
+            const int r = blk * (64 / C::CPK) + lane / C::CPK;
+            const int c = (lane % C::CPK) ^ kcswz<C::CPK>(r);
             src = g + (int64_t(row0 + r) * ld + k0 + c * 8) * 2;
         } else {
             const int k = blk * C::RPK + lane / C::CPR;
             const int c = (lane % C::CPR) ^ kswz(k);
             src = g + (int64_t(k0 + k) * ld + row0 + c * 8) * 2;
         }
-        __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(lds + blk * 1024), 16, 0, 0);
+        lds_dma16(src, lds + blk * 1024);
     }
 }
 
-// One MFMA operand fragment: 8 k values (k = 32 s + 8 (lane >> 4) + e) of
-// row/column `rc` of the stage.
-template <int BM>
-__device__ __forceinline__ bf16x8_t frag(const char* __restrict__ lds, bool kc, int rc16, int s, int lane) {
-    if (kc) {
+// One MFMA operand fragment (8 k values k = 32 s + 8 (lane >> 4) + e of
+// row/column rc16 + (lane & 15)) from one operand stage.
+template <int BM, int BK, bool KC>
+__device__ __forceinline__ bf16x8_t frag(const char* __restrict__ lds, int rc16, int s, int lane) {
+    using C = BfCfg<BM, BK>;
+    if (KC) {
         const int r = rc16 + (lane & 15);
-        const int c = (4 * s + (lane >> 4)) ^ (r & 7);
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lds + r * 128 + c * 16));
+        const int c = (4 * s + (lane >> 4)) ^ kcswz<C::CPK>(r);
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(lds + r * (C::CPK * 16) + c * 16));
     }
     const int i = lane & 15;
     const int n = rc16 + 4 * (i & 3);
@@ -592,8 +636,60 @@ __device__ __forceinline__ bf16x8_t frag(const char* __restrict__ lds, bool kc, 
         const char* p = lds + k * (BM * 2) + c * 16 + (n & 7) * 2;
         h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4_t*)(p));
     }
-    const i16x4_t lo = h[0], hi = h[1];
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int BM, int BK, bool AKC, bool BKC>
+__device__ __forceinline__ void issue_stage(char* __restrict__ st, const Operands& op, int row_a0, int row_b0, int k0,
+                                            int wave, int lane) {
+    issue_operand<BM, BK, AKC>(st, op.a, op.lda, row_a0, k0, wave, lane);
+    issue_operand<BM, BK, BKC>(st + BfCfg<BM, BK>::OPB, op.b, op.ldb, row_b0, k0, wave, lane);
+}
+
+template <int BM, int BK, bool AKC, bool BKC>
+__device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
+                                         int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI]) {
+    using C = BfCfg<BM, BK>;
+    constexpr int TI = C::TI;
+    const int wr = (wave >> 1) * C::WT, wc = (wave & 1) * C::WT;
+    const int nk = (op.K + C::BK - 1) / C::BK;
+    // prologue: stages 0 .. NST-2
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+        if (s < nk) issue_stage<BM, BK, AKC, BKC>(smem + s * C::STB, op, row_a0, row_b0, s * C::BK, wave, lane);
+    for (int kb = 0; kb < nk; ++kb) {
+        // stage kb has landed once at most (stages issued after it) x LPS loads are pending
+        const int ahead = nk - 1 - kb;
+        if (C::NST > 2 && ahead >= 2)
+            vm_wait<(C::NST > 2 ? 2 : 0) * C::LPS>();
+        else if (C::NST > 2 && ahead == 1)
+            vm_wait<(C::NST > 2 ? 1 : 0) * C::LPS>();
+        else
+            vm_wait<0>();
+        __syncthreads();   // every wave's share of stage kb is in LDS; stage kb-1 is free
+        if (kb + C::NST - 1 < nk)
+            issue_stage<BM, BK, AKC, BKC>(smem + ((kb + C::NST - 1) % C::NST) * C::STB, op, row_a0, row_b0,
+                                          (kb + C::NST - 1) * C::BK, wave, lane);
+        const char* sa = smem + (kb % C::NST) * C::STB;
+        const char* sb = sa + C::OPB;
+#pragma unroll
+        for (int s = 0; s < BK / 32; ++s) {
+            bf16x8_t fa[TI], fb[TI];
+#pragma unroll
+            for (int i = 0; i < TI; ++i) fa[i] = frag<BM, BK, AKC>(sa, wr + 16 * i, s, lane);
+#pragma unroll
+            for (int j = 0; j < TI; ++j) fb[j] = frag<BM, BK, BKC>(sb, wc + 16 * j, s, lane);
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TI; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            // issue every fragment read of the step before the MFMAs that consume them
+            constexpr int kReads = TI * ((AKC ? 1 : 2) + (BKC ? 1 : 2));
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, TI * TI, 0);  // MFMAs
+        }
+    }
 }
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -647,184 +743,444 @@ __device__ __forceinline__ f32x4_t u4_at(const MatDesc& md, int64_t r, int64_t c
 // Epilogue through LDS.  Each wave stages its (16 x WT) row bands in fp32 in its
 // own LDS region and reads them back as 4-element runs along rows (row-major
 // pass) or down columns (column-major pass), so global traffic moves in 8- and
-// 16-byte vectors along contiguous rows of the destination.
-template <int KIND, int TI>
-__device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                                const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                                float* __restrict__ stg) {
-    constexpr int WT = TI * 16, LDW = WT + 4;
-    char* const ws = pa.ws;
-    const int it = pa.iter;
-    const int m = md.m, n = md.n;
-    const bool trans = md.trans != 0;
-    const bool nest = pa.nesterov != 0;
-    const bool vio = md.vec_io != 0;
-    const bool gp = (KIND == PH_GRAM || KIND == PH_POLY);
-    const bool diag = gp && t.ti == t.tj;
-    // GRAM/POLY: out (and A for POLY); AXPY: X master / operand copies
-    const int64_t ldq = gp ? md.mp : md.np;
-    uint16_t* out = reinterpret_cast<uint16_t*>(ws + (KIND == PH_GRAM ? md.off_a : md.off_b));
-    const uint16_t* ain = reinterpret_cast<const uint16_t*>(ws + md.off_a);
-    float scl = 1.f;
-    if (KIND == PH_GRAM && it == 1) {
-        const float s = pa.inv_norm[t.mat];
-        scl = s * s;
+// 16-byte vectors along contiguous rows of the destination.  Every global value
+// a band needs is loaded before the band is staged, and the next band's loads
+// are issued before the current band is stored, so each lane keeps a band's
+// worth of loads in flight.
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so
+// array indices derived from I stay constant whatever the unroller decides.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
     }
-    const float alpha = (it == 1) ? pa.inv_norm[t.mat] : 1.f;
-    float* xm = reinterpret_cast<float*>(ws + md.off_xm);
-    uint16_t* xb_next = reinterpret_cast<uint16_t*>(ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
-    const float wdec = 1.f - pa.lr * pa.wd;
-    const float step = pa.lr * md.shape_scale;
-    const bool row_pass = gp || KIND == PH_AXPY || !trans;
-    const bool col_pass = gp || (KIND == PH_AXPY_LAST && trans);
-    const int g = lane >> 4, c16 = lane & 15;
+}
 
+template <int TI>
+struct EpiGeom {
+    static constexpr int WT = TI * 16;    // wave tile edge
+    static constexpr int LDW = WT + 4;    // padded LDS row (floats)
+    static constexpr int NQ = WT / 16;    // 4-element runs per lane per band
+};
+
+template <int TI>
+__device__ __forceinline__ void stage_band(float* __restrict__ stg, const f32x4_t (&acc)[TI][TI], int i, int lane) {
+    constexpr int LDW = EpiGeom<TI>::LDW;
+    const int g = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+    for (int j = 0; j < TI; ++j)
 #pragma unroll
-        for (int j = 0; j < TI; ++j)
+        for (int e = 0; e < 4; ++e) stg[(4 * g + e) * LDW + 16 * j + c16] = acc[i][j][e];
+}
+
+// Row-major pass geometry: run q of a lane covers band row lr, columns lc..lc+3.
+template <int TI>
+__device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
+    constexpr int WT = EpiGeom<TI>::WT;
+    const int idx = q * 256 + lane * 4;
+    lr = idx / WT;
+    lc = idx % WT;
+}
+// Column-major pass geometry: run q of a lane covers band rows 4 quad..+3 of column lc.
+template <int TI>
+__device__ __forceinline__ void col_run(int q, int lane, int& quad, int& lc) {
+    constexpr int WT = EpiGeom<TI>::WT;
+    const int task = q * 64 + lane;
+    lc = task % WT;
+    quad = task / WT;
+}
+
+// ---- AXPY (not last): X' = alpha (a X + B X), fp32 master and bf16 operand copy
+struct AxpyCtx {
+    float* xm;
+    uint16_t* xb_next;
+    int64_t ldq;
+    int m, n, it;
+    bool trans, nest, vio;
+    float alpha, a, beta;
+};
+
+template <int TI, bool FIRST>
+__device__ __forceinline__ void axpy_load(const MatDesc& md, const AxpyCtx& x, int row0, int col0, int lane, int band,
+                                          f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) stg[(4 * g + e) * LDW + 16 * j + c16] = acc[i][j][e];
-        const int rb = row0 + 16 * i;
-        if (row_pass) {
-#pragma unroll 2
-            for (int q = 0; q < WT / 16; ++q) {
-                const int idx = q * 256 + lane * 4;
-                const int lr = idx / WT, lc = idx % WT;
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * LDW + lc);
-                const int r = rb + lr, c = col0 + lc;
-                if (gp) {
-                    if (r >= m) continue;
-                    int nv = m - c;                 // columns inside the matrix
-                    nv = nv > 4 ? 4 : nv;
-                    int first = 0;                  // diagonal tiles keep r <= c
-                    if (diag && r > c) first = r - c;
-                    if (nv <= first) continue;
-                    const int64_t o = int64_t(r) * ldq + c;
-                    f32x4_t w;
-                    if (KIND == PH_GRAM) {
-                        w = v * scl;
-                    } else {
-                        const f32x4_t a4 = (nv == 4) ? ld4_bf16(ain + o) : ld4_io(ain, o, 0, false, nv);
-                        w = pa.b * a4 + pa.c * v;
-                    }
-                    if (nv == 4 && first == 0)
-                        st4_bf16(out + o, w);
-                    else
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2)
-                            if (q2 >= first && q2 < nv) out[o + q2] = f32_to_bf16(w[q2]);
+    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
+        int lr, lc;
+        row_run<TI>(q, lane, lr, lc);
+        const int r = row0 + 16 * band + lr, c = col0 + lc;
+        if (!FIRST) {
+            mst[q] = *reinterpret_cast<const f32x4_t*>(x.xm + int64_t(r) * x.ldq + c);   // padded: in bounds
+        } else {
+            mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (r < x.m && c < x.n) {
+                int nv = x.n - c;
+                nv = nv > 4 ? 4 : nv;
+                if (!x.trans) {
+                    mst[q] = u4_at(md, r, c, x.beta, x.nest, x.vio && nv == 4, nv);
                 } else {
-                    if (r >= m || c >= n) continue;
-                    int nv = n - c;
-                    nv = nv > 4 ? 4 : nv;
-                    f32x4_t master;
-                    if (it == 1)
-                        master = trans ? f32x4_t{u_at(md, c, r, pa.beta, nest),
-                                                 nv > 1 ? u_at(md, c + 1, r, pa.beta, nest) : 0.f,
-                                                 nv > 2 ? u_at(md, c + 2, r, pa.beta, nest) : 0.f,
-                                                 nv > 3 ? u_at(md, c + 3, r, pa.beta, nest) : 0.f}
-                                       : u4_at(md, r, c, pa.beta, nest, vio && nv == 4, nv);
-                    else
-                        master = *reinterpret_cast<const f32x4_t*>(xm + int64_t(r) * ldq + c);  // padded: in bounds
-                    f32x4_t x = alpha * (pa.a * master + v);
-                    if (KIND == PH_AXPY) {
-                        const int64_t o = int64_t(r) * ldq + c;
-                        if (nv == 4) {
-                            *reinterpret_cast<f32x4_t*>(xm + o) = x;
-                            st4_bf16(xb_next + o, x);
-                        } else {
 #pragma unroll
-                            for (int q2 = 0; q2 < 4; ++q2)
-                                if (q2 < nv) {
-                                    xm[o + q2] = x[q2];
-                                    xb_next[o + q2] = f32_to_bf16(x[q2]);
-                                }
-                        }
-                    } else {  // last iteration, stored orientation = NS orientation
-                        const bool vec = vio && nv == 4;
-                        if (md.has_param) {
-                            const int64_t pi = int64_t(r) * md.ld_param + c;
-                            const f32x4_t w = ld4_io(md.param, pi, md.io_dtype, vec, nv);
-                            f32x4_t wn;
-#pragma unroll
-                            for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-step, x[q2], w[q2] * wdec);
-                            st4_io(md.param, pi, md.io_dtype, vec, nv, wn);
-                        }
-                        if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, x);
-                    }
-                }
-            }
-        }
-        if (col_pass) {
-#pragma unroll 2
-            for (int q = 0; q < WT / 16; ++q) {
-                const int task = q * 64 + lane;
-                const int lc = task % WT, quad = task / WT;
-                const int r = rb + 4 * quad, c = col0 + lc;   // elements (r..r+3, c)
-                f32x4_t v;
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(4 * quad + q2) * LDW + lc];
-                if (gp) {
-                    // mirror: (r + q2, c) -> (c, r + q2); diagonal tiles mirror only r + q2 < c
-                    if (c >= m) continue;
-                    int nv = m - r;
-                    nv = nv > 4 ? 4 : nv;
-                    if (diag) {
-                        const int lim = c - r;        // q2 < lim  <=>  r + q2 < c
-                        nv = nv < lim ? nv : lim;
-                    }
-                    if (nv <= 0) continue;
-                    const int64_t o = int64_t(c) * ldq + r;
-                    f32x4_t w;
-                    if (KIND == PH_GRAM) {
-                        w = v * scl;
-                    } else {
-                        const f32x4_t a4 = (nv == 4) ? ld4_bf16(ain + o) : ld4_io(ain, o, 0, false, nv);  // A symmetric
-                        w = pa.b * a4 + pa.c * v;
-                    }
-                    if (nv == 4)
-                        st4_bf16(out + o, w);
-                    else
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2)
-                            if (q2 < nv) out[o + q2] = f32_to_bf16(w[q2]);
-                } else {
-                    // last iteration of a transposed matrix: NS (r + q2, c) is stored (c, r + q2)
-                    if (c >= n || r >= m) continue;
-                    int nv = m - r;
-                    nv = nv > 4 ? 4 : nv;
-                    const bool vec = vio && nv == 4;
-                    f32x4_t master;
-                    if (it == 1) {
-                        master = u4_at(md, c, r, pa.beta, nest, vec, nv);
-                    } else {
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2) master[q2] = xm[int64_t(r + q2) * ldq + c];  // padded rows
-                    }
-                    const f32x4_t x = alpha * (pa.a * master + v);
-                    if (md.has_param) {
-                        const int64_t pi = int64_t(c) * md.ld_param + r;
-                        const f32x4_t w = ld4_io(md.param, pi, md.io_dtype, vec, nv);
-                        f32x4_t wn;
-#pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-step, x[q2], w[q2] * wdec);
-                        st4_io(md.param, pi, md.io_dtype, vec, nv, wn);
-                    }
-                    if (md.upd) st4_io(md.upd, int64_t(c) * md.ld_upd + r, 1, vec, nv, x);
+                    for (int q2 = 0; q2 < 4; ++q2)
+                        if (q2 < nv) mst[q][q2] = u_at(md, c + q2, r, x.beta, x.nest);
                 }
             }
         }
     }
 }
 
-template <int KIND, int BM>
+template <int TI>
+__device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
+                                           int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
+    using E = EpiGeom<TI>;
+#pragma unroll
+    for (int q = 0; q < E::NQ; ++q) {
+        int lr, lc;
+        row_run<TI>(q, lane, lr, lc);
+        const int r = row0 + 16 * band + lr, c = col0 + lc;
+        if (r >= x.m || c >= x.n) continue;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
+        const f32x4_t o = x.alpha * (x.a * mst[q] + v);
+        const int64_t off = int64_t(r) * x.ldq + c;
+        if (c + 4 <= x.n) {
+            *reinterpret_cast<f32x4_t*>(x.xm + off) = o;
+            st4_bf16(x.xb_next + off, o);
+        } else {
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+                if (c + q2 < x.n) {
+                    x.xm[off + q2] = o[q2];
+                    x.xb_next[off + q2] = f32_to_bf16(o[q2]);
+                }
+        }
+    }
+}
+
+// First iteration of a transposed matrix: the master term comes from the
+// stored-orientation u, so runs go down NS columns (= along stored rows):
+// run q covers NS rows r..r+3 of column c, i.e. stored (c, r..r+3).
+template <int TI>
+__device__ __forceinline__ void axpy_load_col(const MatDesc& md, const AxpyCtx& x, int row0, int col0, int lane,
+                                              int band, f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
+#pragma unroll
+    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
+        int quad, lc;
+        col_run<TI>(q, lane, quad, lc);
+        const int r = row0 + 16 * band + 4 * quad, c = col0 + lc;
+        mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (c < x.n && r < x.m) {
+            int nv = x.m - r;
+            nv = nv > 4 ? 4 : nv;
+            mst[q] = u4_at(md, c, r, x.beta, x.nest, x.vio && nv == 4, nv);
+        }
+    }
+}
+
+template <int TI>
+__device__ __forceinline__ void axpy_store_col(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
+                                               int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
+    using E = EpiGeom<TI>;
+#pragma unroll
+    for (int q = 0; q < E::NQ; ++q) {
+        int quad, lc;
+        col_run<TI>(q, lane, quad, lc);
+        const int r = row0 + 16 * band + 4 * quad, c = col0 + lc;
+        if (c >= x.n || r >= x.m) continue;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            if (r + q2 >= x.m) break;
+            const float v = stg[(4 * quad + q2) * E::LDW + lc];
+            const float o = x.alpha * (x.a * mst[q][q2] + v);
+            const int64_t off = int64_t(r + q2) * x.ldq + c;
+            x.xm[off] = o;
+            x.xb_next[off] = f32_to_bf16(o);
+        }
+    }
+}
+
+template <int TI, bool FIRST>
+__device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                         float* __restrict__ stg) {
+    constexpr int NQ = EpiGeom<TI>::NQ;
+    AxpyCtx x;
+    x.it = pa.iter;
+    x.xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
+    x.xb_next = reinterpret_cast<uint16_t*>(pa.ws + (((x.it - 1) & 1) ? md.off_xb1 : md.off_xb0));
+    x.ldq = md.np;
+    x.m = md.m;
+    x.n = md.n;
+    x.trans = md.trans != 0;
+    x.nest = pa.nesterov != 0;
+    x.vio = md.vec_io != 0;
+    x.alpha = (x.it == 1) ? pa.inv_norm[t.mat] : 1.f;
+    x.a = pa.a;
+    x.beta = pa.beta;
+    f32x4_t mst[2][NQ];
+    if (FIRST && x.trans) {
+        axpy_load_col<TI>(md, x, row0, col0, lane, 0, mst[0]);
+        static_for<0, TI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i + 1 < TI) axpy_load_col<TI>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1]);
+            stage_band<TI>(stg, acc, i, lane);
+            axpy_store_col<TI>(x, stg, row0, col0, lane, i, mst[i & 1]);
+        });
+        return;
+    }
+    axpy_load<TI, FIRST>(md, x, row0, col0, lane, 0, mst[0]);
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < TI) axpy_load<TI, FIRST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1]);   // one band ahead
+        stage_band<TI>(stg, acc, i, lane);
+        axpy_store<TI>(x, stg, row0, col0, lane, i, mst[i & 1]);
+    });
+}
+
+// ---- last iteration: O = alpha (a X + B X); W = W (1 - lr wd) - lr s O and
+// the optional fp32 copy of O, in the stored orientation (column-major pass for
+// transposed matrices, so stored rows stay contiguous).
+struct LastCtx {
+    const float* xm;
+    int64_t ldq;
+    int m, n, it;
+    bool trans, nest, vio;
+    float alpha, a, beta, wdec, step;
+};
+
+// run q of band `band`: NS (r, c), stored (sr, sc..sc+nv-1)
+template <int TI>
+__device__ __forceinline__ void last_locate(const LastCtx& x, int row0, int col0, int lane, int band, int q, int& r,
+                                            int& c, int64_t& sr, int64_t& sc, int& nv) {
+    if (!x.trans) {
+        int lr, lc;
+        row_run<TI>(q, lane, lr, lc);
+        r = row0 + 16 * band + lr;
+        c = col0 + lc;
+        sr = r;
+        sc = c;
+        nv = (r < x.m) ? x.n - c : 0;
+    } else {
+        int quad, lc;
+        col_run<TI>(q, lane, quad, lc);
+        r = row0 + 16 * band + 4 * quad;
+        c = col0 + lc;
+        sr = c;
+        sc = r;
+        nv = (c < x.n) ? x.m - r : 0;
+    }
+    nv = nv > 4 ? 4 : (nv < 0 ? 0 : nv);
+}
+
+template <int TI, bool FIRST>
+__device__ __forceinline__ void last_load(const MatDesc& md, const LastCtx& x, int row0, int col0, int lane, int band,
+                                          f32x4_t (&mst)[EpiGeom<TI>::NQ], f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
+#pragma unroll
+    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
+        int r, c, nv;
+        int64_t sr, sc;
+        last_locate<TI>(x, row0, col0, lane, band, q, r, c, sr, sc, nv);
+        mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        wv[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (nv <= 0) continue;
+        const bool vec = x.vio && nv == 4;
+        if (FIRST) {
+            mst[q] = u4_at(md, sr, sc, x.beta, x.nest, vec, nv);
+        } else if (!x.trans) {
+            mst[q] = *reinterpret_cast<const f32x4_t*>(x.xm + int64_t(r) * x.ldq + c);
+        } else {
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) mst[q][q2] = x.xm[int64_t(r + q2) * x.ldq + c];   // padded rows
+        }
+        if (md.has_param) wv[q] = ld4_io(md.param, sr * md.ld_param + sc, md.io_dtype, vec, nv);
+    }
+}
+
+template <int TI>
+__device__ __forceinline__ void last_store(const MatDesc& md, const LastCtx& x, const float* __restrict__ stg, int row0,
+                                           int col0, int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ],
+                                           const f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
+    using E = EpiGeom<TI>;
+#pragma unroll
+    for (int q = 0; q < E::NQ; ++q) {
+        int r, c, nv;
+        int64_t sr, sc;
+        last_locate<TI>(x, row0, col0, lane, band, q, r, c, sr, sc, nv);
+        if (nv <= 0) continue;
+        f32x4_t v;
+        const int br = r - row0 - 16 * band, lc = c - col0;
+        if (!x.trans) {
+            v = *reinterpret_cast<const f32x4_t*>(stg + br * E::LDW + lc);
+        } else {
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(br + q2) * E::LDW + lc];
+        }
+        const f32x4_t o = x.alpha * (x.a * mst[q] + v);
+        const bool vec = x.vio && nv == 4;
+        if (md.has_param) {
+            f32x4_t w;
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) w[q2] = fmaf(-x.step, o[q2], wv[q][q2] * x.wdec);
+            st4_io(md.param, sr * md.ld_param + sc, md.io_dtype, vec, nv, w);
+        }
+        if (md.upd) st4_io(md.upd, sr * md.ld_upd + sc, 1, vec, nv, o);
+    }
+}
+
+template <int TI, bool FIRST>
+__device__ __forceinline__ void epi_last(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                         float* __restrict__ stg) {
+    constexpr int NQ = EpiGeom<TI>::NQ;
+    LastCtx x;
+    x.it = pa.iter;
+    x.xm = reinterpret_cast<const float*>(pa.ws + md.off_xm);
+    x.ldq = md.np;
+    x.m = md.m;
+    x.n = md.n;
+    x.trans = md.trans != 0;
+    x.nest = pa.nesterov != 0;
+    x.vio = md.vec_io != 0;
+    x.alpha = (x.it == 1) ? pa.inv_norm[t.mat] : 1.f;
+    x.a = pa.a;
+    x.beta = pa.beta;
+    x.wdec = 1.f - pa.lr * pa.wd;
+    x.step = pa.lr * md.shape_scale;
+    f32x4_t mst[2][NQ], wv[2][NQ];
+    last_load<TI, FIRST>(md, x, row0, col0, lane, 0, mst[0], wv[0]);
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < TI) last_load<TI, FIRST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1], wv[(i + 1) & 1]);
+        stage_band<TI>(stg, acc, i, lane);
+        last_store<TI>(md, x, stg, row0, col0, lane, i, mst[i & 1], wv[i & 1]);
+    });
+}
+
+// ---- GRAM (A = s^2 X X^T) and POLY (B = b A + c A A): upper triangle written
+// to (r, c) by the row-major pass and mirrored to (c, r) by the column-major
+// pass (diagonal tiles: r <= c, and r < c for the mirror).
+struct SymCtx {
+    uint16_t* out;
+    const uint16_t* ain;
+    int64_t ldq;
+    int m;
+    bool diag;
+    float scl, b, c;
+};
+
+// A values a band needs (POLY): rows r, columns c..c+3 (row pass) and, by
+// symmetry, A[c][r..r+3] (mirror pass); padded, so always in bounds
+template <int TI>
+__device__ __forceinline__ void sym_load(const SymCtx& x, int row0, int col0, int lane, int band,
+                                         f32x4_t (&ar)[EpiGeom<TI>::NQ], f32x4_t (&am)[EpiGeom<TI>::NQ]) {
+#pragma unroll
+    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
+        int lr, lc, quad, lc2;
+        row_run<TI>(q, lane, lr, lc);
+        col_run<TI>(q, lane, quad, lc2);
+        ar[q] = ld4_bf16(x.ain + int64_t(row0 + 16 * band + lr) * x.ldq + col0 + lc);
+        am[q] = ld4_bf16(x.ain + int64_t(col0 + lc2) * x.ldq + row0 + 16 * band + 4 * quad);
+    }
+}
+
+template <int TI, bool POLY>
+__device__ __forceinline__ void sym_store(const SymCtx& x, const float* __restrict__ stg, int row0, int col0, int lane,
+                                          int band, const f32x4_t (&ar)[EpiGeom<TI>::NQ],
+                                          const f32x4_t (&am)[EpiGeom<TI>::NQ]) {
+    using E = EpiGeom<TI>;
+    const int rb = row0 + 16 * band;
+#pragma unroll
+    for (int q = 0; q < E::NQ; ++q) {   // row-major pass: (r, c..c+3)
+        int lr, lc;
+        row_run<TI>(q, lane, lr, lc);
+        const int r = rb + lr, c = col0 + lc;
+        if (r >= x.m) continue;
+        int nv = x.m - c;
+        nv = nv > 4 ? 4 : nv;
+        const int first = (x.diag && r > c) ? r - c : 0;
+        if (nv <= first) continue;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
+        const f32x4_t w = POLY ? x.b * ar[q] + x.c * v : v * x.scl;
+        const int64_t o = int64_t(r) * x.ldq + c;
+        if (nv == 4 && first == 0)
+            st4_bf16(x.out + o, w);
+        else
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+                if (q2 >= first && q2 < nv) x.out[o + q2] = f32_to_bf16(w[q2]);
+    }
+#pragma unroll
+    for (int q = 0; q < E::NQ; ++q) {   // mirror pass: (r..r+3, c) -> (c, r..r+3)
+        int quad, lc;
+        col_run<TI>(q, lane, quad, lc);
+        const int r = rb + 4 * quad, c = col0 + lc;
+        if (c >= x.m) continue;
+        int nv = x.m - r;
+        nv = nv > 4 ? 4 : nv;
+        if (x.diag) nv = nv < c - r ? nv : c - r;
+        if (nv <= 0) continue;
+        f32x4_t v;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(4 * quad + q2) * E::LDW + lc];
+        const f32x4_t w = POLY ? x.b * am[q] + x.c * v : v * x.scl;
+        const int64_t o = int64_t(c) * x.ldq + r;
+        if (nv == 4)
+            st4_bf16(x.out + o, w);
+        else
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+                if (q2 < nv) x.out[o + q2] = f32_to_bf16(w[q2]);
+    }
+}
+
+template <int KIND, int TI>
+__device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                        const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                        float* __restrict__ stg) {
+    constexpr int NQ = EpiGeom<TI>::NQ;
+    constexpr bool POLY = KIND == PH_POLY;
+    SymCtx x;
+    x.out = reinterpret_cast<uint16_t*>(pa.ws + (KIND == PH_GRAM ? md.off_a : md.off_b));
+    x.ain = reinterpret_cast<const uint16_t*>(pa.ws + md.off_a);
+    x.ldq = md.mp;
+    x.m = md.m;
+    x.diag = t.ti == t.tj;
+    x.scl = 1.f;
+    if (KIND == PH_GRAM && pa.iter == 1) {
+        const float sn = pa.inv_norm[t.mat];
+        x.scl = sn * sn;
+    }
+    x.b = pa.b;
+    x.c = pa.c;
+    f32x4_t ar[2][NQ], am[2][NQ];
+    if (POLY) sym_load<TI>(x, row0, col0, lane, 0, ar[0], am[0]);
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (POLY && i + 1 < TI) sym_load<TI>(x, row0, col0, lane, i + 1, ar[(i + 1) & 1], am[(i + 1) & 1]);
+        stage_band<TI>(stg, acc, i, lane);
+        sym_store<TI, POLY>(x, stg, row0, col0, lane, i, ar[i & 1], am[i & 1]);
+    });
+}
+
+template <int KIND, int TI, bool FIRST>
+__device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                                const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                                float* __restrict__ stg) {
+    if (KIND == PH_AXPY)
+        epi_axpy<TI, FIRST>(md, t, pa, acc, row0, col0, lane, stg);
+    else if (KIND == PH_AXPY_LAST)
+        epi_last<TI, FIRST>(md, t, pa, acc, row0, col0, lane, stg);
+    else
+        epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, stg);
+}
+
+// FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
+// term recomputed from the caller's momentum and gradient).
+template <int KIND, int BM, bool FIRST>
 __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
                                                             const MatDesc* __restrict__ mats, PhaseArgs pa,
                                                             int n_tiles) {
-    using C = BfCfg<BM>;
+    using C = BfCfg<BM, kBK>;
     constexpr int TI = C::TI, WT = C::WT;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * C::OPB];   // [stage][A | B]
+    __shared__ __attribute__((aligned(1024))) char smem[C::NST * C::STB];
 
     const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
     const MatDesc& md = mats[t.mat];
@@ -841,37 +1197,17 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 #pragma unroll
         for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (op.K + C::BK - 1) / C::BK;
-    lds_fill<BM>(smem, op.a, op.lda, op.a_kc, row_a0, 0, wave, lane);
-    lds_fill<BM>(smem + C::OPB, op.b, op.ldb, op.b_kc, row_b0, 0, wave, lane);
+    // operand layouts that occur: GRAM (kc, kc) or, for X0 = U^T, (ks, ks);
+    // POLY (kc, kc); AXPY (kc, ks) or, for X0 = U^T, (kc, kc)
+    if (KIND == PH_POLY || (op.a_kc && op.b_kc))
+        mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+    else if (KIND == PH_GRAM)
+        mainloop<BM, kBK, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+    else
+        mainloop<BM, kBK, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
 
-    for (int kb = 0; kb < nk; ++kb) {
-        char* cur = smem + (kb & 1) * 2 * C::OPB;
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of stage kb have landed
-        __syncthreads();                 // ... and every wave's; stage kb-1 is free
-        if (kb + 1 < nk) {
-            char* nxt = smem + ((kb + 1) & 1) * 2 * C::OPB;
-            lds_fill<BM>(nxt, op.a, op.lda, op.a_kc, row_a0, (kb + 1) * C::BK, wave, lane);
-            lds_fill<BM>(nxt + C::OPB, op.b, op.ldb, op.b_kc, row_b0, (kb + 1) * C::BK, wave, lane);
-        }
-        const char* sa = cur;
-        const char* sb = cur + C::OPB;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8_t fa[TI], fb[TI];
-#pragma unroll
-            for (int i = 0; i < TI; ++i) fa[i] = frag<BM>(sa, op.a_kc, wr + 16 * i, s, lane);
-#pragma unroll
-            for (int j = 0; j < TI; ++j) fb[j] = frag<BM>(sb, op.b_kc, wc + 16 * j, s, lane);
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int j = 0; j < TI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-    }
     __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-    epilogue_staged<KIND, TI>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
+    epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
                               reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
 }
 
@@ -932,15 +1268,28 @@ hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* pa
     return hipGetLastError();
 }
 
+template <int KIND, int BM>
+static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s) {
+    // only AXPY epilogues differ on the first iteration
+    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+        if (first) {
+            hipLaunchKernelGGL((ns_gemm_bf16<KIND, BM, true>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a,
+                               n_tiles);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((ns_gemm_bf16<KIND, BM, false>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
+}
+
 template <int KIND>
 static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
                         hipStream_t s) {
     if (f32c)
         hipLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a);
     else if (tile == 256)
-        hipLaunchKernelGGL((ns_gemm_bf16<KIND, 256>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
+        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s);
     else
-        hipLaunchKernelGGL((ns_gemm_bf16<KIND, 128>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
+        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
