@@ -242,11 +242,13 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
 
     // Newton-Schulz tile lists.  One tile edge per phase for the whole call:
     // the large tile when it still yields a couple of workgroups per CU.
+    // GRAM/POLY: upper triangle of the m x m product; AXPY: the stored R x C
+    // shape (X is kept in the caller's orientation, transposed matrices as X^T)
     auto count_tiles = [&](int T, bool gram) {
         int64_t c = 0;
         for (const MatDesc& d : geom) {
-            const int64_t tm = (d.m + T - 1) / T, tn = (d.n + T - 1) / T;
-            c += gram ? tm * (tm + 1) / 2 : tm * tn;
+            const int64_t tm = (d.m + T - 1) / T;
+            c += gram ? tm * (tm + 1) / 2 : int64_t((d.R + T - 1) / T) * ((d.C + T - 1) / T);
         }
         return c;
     };
@@ -268,8 +270,9 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         });
         for (int i : ord) {
             const MatDesc& d = geom[i];
-            // GRAM/POLY outputs are m x m (upper triangle); AXPY outputs are m x n
-            const int tm = (d.m + T - 1) / T, tn = gram ? tm : (d.n + T - 1) / T;
+            // GRAM/POLY outputs are m x m (upper triangle); AXPY outputs are R x C
+            const int tm = gram ? (d.m + T - 1) / T : (d.R + T - 1) / T;
+            const int tn = gram ? tm : (d.C + T - 1) / T;
             for (int a0 = 0; a0 < tm; a0 += 4)
                 for (int b = 0; b < tn; ++b)
                     for (int a = a0; a < std::min(tm, a0 + 4); ++a)
@@ -286,7 +289,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     }
     for (const Tile& t : axpy) {
         const MatDesc& d = geom[t.mat];
-        if ((t.ti + 1) * axpy_tile > d.mp || (t.tj + 1) * axpy_tile > d.np)
+        if ((t.ti + 1) * axpy_tile > d.Rp || (t.tj + 1) * axpy_tile > d.Cp)
             return fail(h, MUON_ERR_HIP, "internal: axpy tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
     }
 

@@ -320,44 +320,49 @@ struct Operands {
     int64_t off_cur;   // workspace offset of the current X operand copy
 };
 
+// X lives in the caller's stored orientation throughout (R x C, leading
+// dimension Cp): for a transposed matrix (R > C) the iteration variable
+// X = U^T is kept as X^T.  Then
+//   GRAM  A = X X^T      : rows of X along k (kc), or columns of X^T (ks)
+//   POLY  A A = A A^T    : rows of A (A symmetric)
+//   AXPY  X' = a X + B X : rows of B with columns of X (ks); transposed
+//                          X'^T = a X^T + X^T B: rows of X^T with rows of B
+//                          (B symmetric), output tile in the stored orientation.
 template <int KIND>
 __device__ __forceinline__ Operands resolve_operands(const MatDesc& md, const PhaseArgs& pa) {
     Operands o;
     const char* ws = pa.ws;
     const int it = pa.iter;
-    // current X: the momentum pass's copy of u (stored orientation) on the first
-    // iteration, afterwards the operand copy written by the previous iteration
+    // current X: the momentum pass's copy of u on the first iteration,
+    // afterwards the operand copy written by the previous iteration
     o.off_cur = (it == 1) ? md.off_u : (((it - 2) & 1) ? md.off_xb1 : md.off_xb0);
+    const bool trans = md.trans != 0;
     if (KIND == PH_GRAM) {
-        // A = X X^T: both operands are rows of X
         o.K = md.n;
         o.a = o.b = ws + o.off_cur;
-        if (it == 1) {
-            o.lda = o.ldb = md.Cp;
-            o.a_kc = o.b_kc = !md.trans;   // X0 = U^T when transposed
-        } else {
-            o.lda = o.ldb = md.np;
-            o.a_kc = o.b_kc = true;
-        }
+        o.lda = o.ldb = md.Cp;
+        o.a_kc = o.b_kc = !trans;
     } else if (KIND == PH_POLY) {
-        // A A = A A^T (A symmetric): both operands are rows of A
         o.K = md.m;
         o.a = o.b = ws + md.off_a;
         o.lda = o.ldb = md.mp;
         o.a_kc = o.b_kc = true;
     } else {
-        // B X: rows of B, columns of X (X^T rows when X0 = U^T)
         o.K = md.m;
-        o.a = ws + md.off_b;
-        o.lda = md.mp;
-        o.a_kc = true;
-        o.b = ws + o.off_cur;
-        if (it == 1) {
+        if (!trans) {
+            o.a = ws + md.off_b;
+            o.lda = md.mp;
+            o.a_kc = true;
+            o.b = ws + o.off_cur;
             o.ldb = md.Cp;
-            o.b_kc = md.trans != 0;
-        } else {
-            o.ldb = md.np;
             o.b_kc = false;
+        } else {
+            o.a = ws + o.off_cur;
+            o.lda = md.Cp;
+            o.a_kc = true;
+            o.b = ws + md.off_b;
+            o.ldb = md.mp;
+            o.b_kc = true;
         }
     }
     return o;
@@ -402,11 +407,11 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
                     }
                 }
     } else {
-        const int m = md.m, n = md.n;
-        const int64_t ldx = md.np;
+        // AXPY output tiles cover the stored R x C shape (see resolve_operands)
+        const int R = md.R, C = md.C;
+        const int64_t ldx = md.Cp;
         const float alpha = (it == 1) ? pa.inv_norm[t.mat] : 1.f;
         const bool nest = pa.nesterov != 0;
-        const bool trans = md.trans != 0;
         const float* xm = reinterpret_cast<const float*>(ws + (F32 ? off_cur : md.off_xm));
         float* xm_out = reinterpret_cast<float*>(ws + md.off_xm);
         char* xb_next = ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0);
@@ -419,20 +424,19 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = gr0 + 16 * i + e, c = gc0 + 16 * j;
-                    if (r < m && c < n) {
-                        const int64_t sr = trans ? c : r, sc = trans ? r : c;  // stored coordinates
-                        const float master = (it == 1) ? u_at(md, sr, sc, pa.beta, nest) : xm[int64_t(r) * ldx + c];
+                    if (r < R && c < C) {
+                        const float master = (it == 1) ? u_at(md, r, c, pa.beta, nest) : xm[int64_t(r) * ldx + c];
                         const float v = alpha * fmaf(pa.a, master, acc[i][j][e]);
                         if (KIND == PH_AXPY) {
                             if (!F32) xm_out[int64_t(r) * ldx + c] = v;
                             store_elem(xb_next, int64_t(r) * ldx + c, ODT, v);
                         } else {
                             if (md.has_param) {
-                                const int64_t pi = sr * md.ld_param + sc;
+                                const int64_t pi = int64_t(r) * md.ld_param + c;
                                 const float w = load_elem(md.param, pi, md.io_dtype);
                                 store_elem(md.param, pi, md.io_dtype, fmaf(-step, v, w * wdec));
                             }
-                            if (md.upd) md.upd[sr * md.ld_upd + sc] = v;
+                            if (md.upd) md.upd[int64_t(r) * md.ld_upd + c] = v;
                         }
                     }
                 }
@@ -791,19 +795,22 @@ __device__ __forceinline__ void col_run(int q, int lane, int& quad, int& lc) {
     quad = task / WT;
 }
 
-// ---- AXPY (not last): X' = alpha (a X + B X), fp32 master and bf16 operand copy
+// ---- AXPY: X' = alpha (a X + B X) on the stored R x C tile grid (see
+// resolve_operands): fp32 master and bf16 operand copy, or on the last
+// iteration O = X' applied to the weight: W = W (1 - lr wd) - lr s O and the
+// optional fp32 copy of O.  Runs are 4 consecutive stored columns of one row.
 struct AxpyCtx {
     float* xm;
     uint16_t* xb_next;
     int64_t ldq;
-    int m, n, it;
-    bool trans, nest, vio;
-    float alpha, a, beta;
+    int R, C;
+    bool nest, vio;
+    float alpha, a, beta, wdec, step;
 };
 
-template <int TI, bool FIRST>
+template <int TI, bool FIRST, bool LAST>
 __device__ __forceinline__ void axpy_load(const MatDesc& md, const AxpyCtx& x, int row0, int col0, int lane, int band,
-                                          f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
+                                          f32x4_t (&mst)[EpiGeom<TI>::NQ], f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
 #pragma unroll
     for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
         int lr, lc;
@@ -813,244 +820,92 @@ __device__ __forceinline__ void axpy_load(const MatDesc& md, const AxpyCtx& x, i
             mst[q] = *reinterpret_cast<const f32x4_t*>(x.xm + int64_t(r) * x.ldq + c);   // padded: in bounds
         } else {
             mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (r < x.m && c < x.n) {
-                int nv = x.n - c;
+            if (r < x.R && c < x.C) {
+                int nv = x.C - c;
                 nv = nv > 4 ? 4 : nv;
-                if (!x.trans) {
-                    mst[q] = u4_at(md, r, c, x.beta, x.nest, x.vio && nv == 4, nv);
-                } else {
-#pragma unroll
-                    for (int q2 = 0; q2 < 4; ++q2)
-                        if (q2 < nv) mst[q][q2] = u_at(md, c + q2, r, x.beta, x.nest);
-                }
+                mst[q] = u4_at(md, r, c, x.beta, x.nest, x.vio && nv == 4, nv);
+            }
+        }
+        if (LAST) {
+            wv[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (md.has_param && r < x.R && c < x.C) {
+                int nv = x.C - c;
+                nv = nv > 4 ? 4 : nv;
+                wv[q] = ld4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, x.vio && nv == 4, nv);
             }
         }
     }
 }
 
-template <int TI>
-__device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
-                                           int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
+template <int TI, bool LAST>
+__device__ __forceinline__ void axpy_store(const MatDesc& md, const AxpyCtx& x, const float* __restrict__ stg,
+                                           int row0, int col0, int lane, int band,
+                                           const f32x4_t (&mst)[EpiGeom<TI>::NQ],
+                                           const f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
     using E = EpiGeom<TI>;
 #pragma unroll
     for (int q = 0; q < E::NQ; ++q) {
         int lr, lc;
         row_run<TI>(q, lane, lr, lc);
         const int r = row0 + 16 * band + lr, c = col0 + lc;
-        if (r >= x.m || c >= x.n) continue;
+        if (r >= x.R || c >= x.C) continue;
+        int nv = x.C - c;
+        nv = nv > 4 ? 4 : nv;
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
         const f32x4_t o = x.alpha * (x.a * mst[q] + v);
-        const int64_t off = int64_t(r) * x.ldq + c;
-        if (c + 4 <= x.n) {
-            *reinterpret_cast<f32x4_t*>(x.xm + off) = o;
-            st4_bf16(x.xb_next + off, o);
+        if (!LAST) {
+            const int64_t off = int64_t(r) * x.ldq + c;
+            if (nv == 4) {
+                *reinterpret_cast<f32x4_t*>(x.xm + off) = o;
+                st4_bf16(x.xb_next + off, o);
+            } else {
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)
+                    if (q2 < nv) {
+                        x.xm[off + q2] = o[q2];
+                        x.xb_next[off + q2] = f32_to_bf16(o[q2]);
+                    }
+            }
         } else {
+            const bool vec = x.vio && nv == 4;
+            if (md.has_param) {
+                f32x4_t w;
 #pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                if (c + q2 < x.n) {
-                    x.xm[off + q2] = o[q2];
-                    x.xb_next[off + q2] = f32_to_bf16(o[q2]);
-                }
+                for (int q2 = 0; q2 < 4; ++q2) w[q2] = fmaf(-x.step, o[q2], wv[q][q2] * x.wdec);
+                st4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vec, nv, w);
+            }
+            if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, o);
         }
     }
 }
 
-// First iteration of a transposed matrix: the master term comes from the
-// stored-orientation u, so runs go down NS columns (= along stored rows):
-// run q covers NS rows r..r+3 of column c, i.e. stored (c, r..r+3).
-template <int TI>
-__device__ __forceinline__ void axpy_load_col(const MatDesc& md, const AxpyCtx& x, int row0, int col0, int lane,
-                                              int band, f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
-#pragma unroll
-    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
-        int quad, lc;
-        col_run<TI>(q, lane, quad, lc);
-        const int r = row0 + 16 * band + 4 * quad, c = col0 + lc;
-        mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (c < x.n && r < x.m) {
-            int nv = x.m - r;
-            nv = nv > 4 ? 4 : nv;
-            mst[q] = u4_at(md, c, r, x.beta, x.nest, x.vio && nv == 4, nv);
-        }
-    }
-}
-
-template <int TI>
-__device__ __forceinline__ void axpy_store_col(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
-                                               int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ]) {
-    using E = EpiGeom<TI>;
-#pragma unroll
-    for (int q = 0; q < E::NQ; ++q) {
-        int quad, lc;
-        col_run<TI>(q, lane, quad, lc);
-        const int r = row0 + 16 * band + 4 * quad, c = col0 + lc;
-        if (c >= x.n || r >= x.m) continue;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-            if (r + q2 >= x.m) break;
-            const float v = stg[(4 * quad + q2) * E::LDW + lc];
-            const float o = x.alpha * (x.a * mst[q][q2] + v);
-            const int64_t off = int64_t(r + q2) * x.ldq + c;
-            x.xm[off] = o;
-            x.xb_next[off] = f32_to_bf16(o);
-        }
-    }
-}
-
-template <int TI, bool FIRST>
+template <int TI, bool FIRST, bool LAST>
 __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                          const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                          float* __restrict__ stg) {
     constexpr int NQ = EpiGeom<TI>::NQ;
     AxpyCtx x;
-    x.it = pa.iter;
+    const int it = pa.iter;
     x.xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
-    x.xb_next = reinterpret_cast<uint16_t*>(pa.ws + (((x.it - 1) & 1) ? md.off_xb1 : md.off_xb0));
-    x.ldq = md.np;
-    x.m = md.m;
-    x.n = md.n;
-    x.trans = md.trans != 0;
+    x.xb_next = reinterpret_cast<uint16_t*>(pa.ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
+    x.ldq = md.Cp;
+    x.R = md.R;
+    x.C = md.C;
     x.nest = pa.nesterov != 0;
     x.vio = md.vec_io != 0;
-    x.alpha = (x.it == 1) ? pa.inv_norm[t.mat] : 1.f;
-    x.a = pa.a;
-    x.beta = pa.beta;
-    f32x4_t mst[2][NQ];
-    if (FIRST && x.trans) {
-        axpy_load_col<TI>(md, x, row0, col0, lane, 0, mst[0]);
-        static_for<0, TI>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i + 1 < TI) axpy_load_col<TI>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1]);
-            stage_band<TI>(stg, acc, i, lane);
-            axpy_store_col<TI>(x, stg, row0, col0, lane, i, mst[i & 1]);
-        });
-        return;
-    }
-    axpy_load<TI, FIRST>(md, x, row0, col0, lane, 0, mst[0]);
-    static_for<0, TI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + 1 < TI) axpy_load<TI, FIRST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1]);   // one band ahead
-        stage_band<TI>(stg, acc, i, lane);
-        axpy_store<TI>(x, stg, row0, col0, lane, i, mst[i & 1]);
-    });
-}
-
-// ---- last iteration: O = alpha (a X + B X); W = W (1 - lr wd) - lr s O and
-// the optional fp32 copy of O, in the stored orientation (column-major pass for
-// transposed matrices, so stored rows stay contiguous).
-struct LastCtx {
-    const float* xm;
-    int64_t ldq;
-    int m, n, it;
-    bool trans, nest, vio;
-    float alpha, a, beta, wdec, step;
-};
-
-// run q of band `band`: NS (r, c), stored (sr, sc..sc+nv-1)
-template <int TI>
-__device__ __forceinline__ void last_locate(const LastCtx& x, int row0, int col0, int lane, int band, int q, int& r,
-                                            int& c, int64_t& sr, int64_t& sc, int& nv) {
-    if (!x.trans) {
-        int lr, lc;
-        row_run<TI>(q, lane, lr, lc);
-        r = row0 + 16 * band + lr;
-        c = col0 + lc;
-        sr = r;
-        sc = c;
-        nv = (r < x.m) ? x.n - c : 0;
-    } else {
-        int quad, lc;
-        col_run<TI>(q, lane, quad, lc);
-        r = row0 + 16 * band + 4 * quad;
-        c = col0 + lc;
-        sr = c;
-        sc = r;
-        nv = (c < x.n) ? x.m - r : 0;
-    }
-    nv = nv > 4 ? 4 : (nv < 0 ? 0 : nv);
-}
-
-template <int TI, bool FIRST>
-__device__ __forceinline__ void last_load(const MatDesc& md, const LastCtx& x, int row0, int col0, int lane, int band,
-                                          f32x4_t (&mst)[EpiGeom<TI>::NQ], f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
-#pragma unroll
-    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
-        int r, c, nv;
-        int64_t sr, sc;
-        last_locate<TI>(x, row0, col0, lane, band, q, r, c, sr, sc, nv);
-        mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        wv[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (nv <= 0) continue;
-        const bool vec = x.vio && nv == 4;
-        if (FIRST) {
-            mst[q] = u4_at(md, sr, sc, x.beta, x.nest, vec, nv);
-        } else if (!x.trans) {
-            mst[q] = *reinterpret_cast<const f32x4_t*>(x.xm + int64_t(r) * x.ldq + c);
-        } else {
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) mst[q][q2] = x.xm[int64_t(r + q2) * x.ldq + c];   // padded rows
-        }
-        if (md.has_param) wv[q] = ld4_io(md.param, sr * md.ld_param + sc, md.io_dtype, vec, nv);
-    }
-}
-
-template <int TI>
-__device__ __forceinline__ void last_store(const MatDesc& md, const LastCtx& x, const float* __restrict__ stg, int row0,
-                                           int col0, int lane, int band, const f32x4_t (&mst)[EpiGeom<TI>::NQ],
-                                           const f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
-    using E = EpiGeom<TI>;
-#pragma unroll
-    for (int q = 0; q < E::NQ; ++q) {
-        int r, c, nv;
-        int64_t sr, sc;
-        last_locate<TI>(x, row0, col0, lane, band, q, r, c, sr, sc, nv);
-        if (nv <= 0) continue;
-        f32x4_t v;
-        const int br = r - row0 - 16 * band, lc = c - col0;
-        if (!x.trans) {
-            v = *reinterpret_cast<const f32x4_t*>(stg + br * E::LDW + lc);
-        } else {
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(br + q2) * E::LDW + lc];
-        }
-        const f32x4_t o = x.alpha * (x.a * mst[q] + v);
-        const bool vec = x.vio && nv == 4;
-        if (md.has_param) {
-            f32x4_t w;
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) w[q2] = fmaf(-x.step, o[q2], wv[q][q2] * x.wdec);
-            st4_io(md.param, sr * md.ld_param + sc, md.io_dtype, vec, nv, w);
-        }
-        if (md.upd) st4_io(md.upd, sr * md.ld_upd + sc, 1, vec, nv, o);
-    }
-}
-
-template <int TI, bool FIRST>
-__device__ __forceinline__ void epi_last(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                         float* __restrict__ stg) {
-    constexpr int NQ = EpiGeom<TI>::NQ;
-    LastCtx x;
-    x.it = pa.iter;
-    x.xm = reinterpret_cast<const float*>(pa.ws + md.off_xm);
-    x.ldq = md.np;
-    x.m = md.m;
-    x.n = md.n;
-    x.trans = md.trans != 0;
-    x.nest = pa.nesterov != 0;
-    x.vio = md.vec_io != 0;
-    x.alpha = (x.it == 1) ? pa.inv_norm[t.mat] : 1.f;
+    x.alpha = FIRST ? pa.inv_norm[t.mat] : 1.f;
     x.a = pa.a;
     x.beta = pa.beta;
     x.wdec = 1.f - pa.lr * pa.wd;
     x.step = pa.lr * md.shape_scale;
     f32x4_t mst[2][NQ], wv[2][NQ];
-    last_load<TI, FIRST>(md, x, row0, col0, lane, 0, mst[0], wv[0]);
+    axpy_load<TI, FIRST, LAST>(md, x, row0, col0, lane, 0, mst[0], wv[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i + 1 < TI) last_load<TI, FIRST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1], wv[(i + 1) & 1]);
+        if constexpr (i + 1 < TI)   // one band ahead
+            axpy_load<TI, FIRST, LAST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1], wv[(i + 1) & 1]);
         stage_band<TI>(stg, acc, i, lane);
-        last_store<TI>(md, x, stg, row0, col0, lane, i, mst[i & 1], wv[i & 1]);
+        axpy_store<TI, LAST>(md, x, stg, row0, col0, lane, i, mst[i & 1], wv[i & 1]);
     });
 }
 
@@ -1165,9 +1020,9 @@ __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t
                                                 const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                                 float* __restrict__ stg) {
     if (KIND == PH_AXPY)
-        epi_axpy<TI, FIRST>(md, t, pa, acc, row0, col0, lane, stg);
+        epi_axpy<TI, FIRST, false>(md, t, pa, acc, row0, col0, lane, stg);
     else if (KIND == PH_AXPY_LAST)
-        epi_last<TI, FIRST>(md, t, pa, acc, row0, col0, lane, stg);
+        epi_axpy<TI, FIRST, true>(md, t, pa, acc, row0, col0, lane, stg);
     else
         epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, stg);
 }
