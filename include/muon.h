@@ -86,7 +86,7 @@ typedef struct muon_hparams {
     float   beta;              /* momentum, 0.95 on the pages */
     float   weight_decay;      /* decoupled: W *= 1 - lr * weight_decay */
     float   eps;               /* added to the Frobenius norm, 1e-7 on the pages */
-    float   a, b, c;           /* quintic coefficients, (3.4445, -4.7750, 2.0315) */
+    float   a, b, c;           /* quintic coefficients, (3.4445, -4.7750, 2.0315); finite, a != 0 */
     int32_t nesterov;          /* 0 or 1 */
     int32_t ns_steps;          /* 0..64; 5 on the pages */
     int32_t compute;           /* muon_compute */
@@ -116,8 +116,8 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
  * signature allocate nothing.
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
  * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
- * momentum aliasing param or grad, ns_steps outside 0..64, reserved != 0,
- * n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
+ * momentum aliasing param or grad, ns_steps outside 0..64, a == 0 or a non-finite
+ * coefficient, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
 muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
                       const muon_hparams *hp, void *stream);
 

@@ -158,6 +158,8 @@ muon_status validate_hp(muon_handle* h, const muon_hparams* hp) {
         return fail(h, MUON_ERR_DTYPE, "unknown compute mode %d", hp->compute);
     if (hp->ns_steps < 0 || hp->ns_steps > kMaxNsSteps)
         return fail(h, MUON_ERR_INVALID_ARG, "ns_steps %d outside 0..%d", hp->ns_steps, kMaxNsSteps);
+    if (!(std::fabs(hp->a) > 0.f) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
+        return fail(h, MUON_ERR_INVALID_ARG, "coefficients must be finite with a != 0");
     if (hp->nesterov != 0 && hp->nesterov != 1)
         return fail(h, MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1, got %d", hp->nesterov);
     return MUON_OK;

@@ -551,7 +551,11 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int BM, int BK_ = 64>
 struct BfCfg {
     static constexpr int BK = BK_;                // k per LDS stage (32 or 64)
-    static constexpr int NST = BK == 64 ? 2 : 4;  // LDS stages (ring)
+    // LDS stages (ring; the epilogue reuses them): 256-wide tiles take the whole
+    // 160 KB (one workgroup per CU), 128-wide tiles stay within 64 KB so two
+    // workgroups share a CU
+    static constexpr int LDS_BUDGET = BM == 256 ? 160 * 1024 : 64 * 1024;
+    static constexpr int NST = LDS_BUDGET / (2 * BM * BK * 2) > 8 ? 8 : LDS_BUDGET / (2 * BM * BK * 2);
     static constexpr int CPK = BK / 8;            // 16-byte chunks per [row][BK] row
     static constexpr int WT = BM / 2;             // wave tile edge
     static constexpr int TI = WT / 16;            // MFMA tiles per wave edge
@@ -650,7 +654,20 @@ __device__ __forceinline__ void issue_stage(char* __restrict__ st, const Operand
     issue_operand<BM, BK, BKC>(st + BfCfg<BM, BK>::OPB, op.b, op.ldb, row_b0, k0, wave, lane);
 }
 
-template <int BM, int BK, bool AKC, bool BKC>
+// SWAP: feed the MFMA (B fragment, A fragment) so that each lane accumulates 4
+// consecutive output columns of one row (acc[i][j][e] = C[16 i + (lane & 15)]
+// [16 j + 4 (lane >> 4) + e]) instead of 4 consecutive rows of one column.
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so
+// array indices derived from I stay constant whatever the unroller decides.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int BM, int BK, bool AKC, bool BKC, bool SWAP>
 __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
                                          int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI]) {
     using C = BfCfg<BM, BK>;
@@ -664,12 +681,11 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
     for (int kb = 0; kb < nk; ++kb) {
         // stage kb has landed once at most (stages issued after it) x LPS loads are pending
         const int ahead = nk - 1 - kb;
-        if (C::NST > 2 && ahead >= 2)
-            vm_wait<(C::NST > 2 ? 2 : 0) * C::LPS>();
-        else if (C::NST > 2 && ahead == 1)
-            vm_wait<(C::NST > 2 ? 1 : 0) * C::LPS>();
-        else
-            vm_wait<0>();
+        const int pend = ahead < C::NST - 2 ? ahead : C::NST - 2;
+        static_for<0, C::NST - 1>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            if (pend == p) vm_wait<p * C::LPS>();
+        });
         __syncthreads();   // every wave's share of stage kb is in LDS; stage kb-1 is free
         if (kb + C::NST - 1 < nk)
             issue_stage<BM, BK, AKC, BKC>(smem + ((kb + C::NST - 1) % C::NST) * C::STB, op, row_a0, row_b0,
@@ -687,7 +703,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                                     : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             // issue every fragment read of the step before the MFMAs that consume them
             constexpr int kReads = TI * ((AKC ? 1 : 2) + (BKC ? 1 : 2));
             __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // LDS reads
@@ -751,15 +768,6 @@ __device__ __forceinline__ f32x4_t u4_at(const MatDesc& md, int64_t r, int64_t c
 // a band needs is loaded before the band is staged, and the next band's loads
 // are issued before the current band is stored, so each lane keeps a band's
 // worth of loads in flight.
-// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so
-// array indices derived from I stay constant whatever the unroller decides.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 
 template <int TI>
 struct EpiGeom {
@@ -852,7 +860,7 @@ __device__ __forceinline__ void axpy_store(const MatDesc& md, const AxpyCtx& x, 
         int nv = x.C - c;
         nv = nv > 4 ? 4 : nv;
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
-        const f32x4_t o = x.alpha * (x.a * mst[q] + v);
+        const f32x4_t o = x.alpha * (x.a * (mst[q] + v));   // acc holds (B / a) X
         if (!LAST) {
             const int64_t off = int64_t(r) * x.ldq + c;
             if (nv == 4) {
@@ -909,7 +917,7 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
     });
 }
 
-// ---- GRAM (A = s^2 X X^T) and POLY (B = b A + c A A): upper triangle written
+// ---- GRAM (A = s^2 X X^T) and POLY (B / a = (b A + c A A) / a): upper triangle written
 // to (r, c) by the row-major pass and mirrored to (c, r) by the column-major
 // pass (diagonal tiles: r <= c, and r < c for the mirror).
 struct SymCtx {
@@ -1003,8 +1011,10 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
         const float sn = pa.inv_norm[t.mat];
         x.scl = sn * sn;
     }
-    x.b = pa.b;
-    x.c = pa.c;
+    // the bf16 AXPY accumulates on top of the unscaled master X, so POLY
+    // stores B / a and AXPY scales the sum by a: X' = a (X + (B / a) X)
+    x.b = pa.b / pa.a;
+    x.c = pa.c / pa.a;
     f32x4_t ar[2][NQ], am[2][NQ];
     if (POLY) sym_load<TI>(x, row0, col0, lane, 0, ar[0], am[0]);
     static_for<0, TI>([&](auto ic) {
@@ -1019,12 +1029,116 @@ template <int KIND, int TI, bool FIRST>
 __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                                 const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                                 float* __restrict__ stg) {
-    if (KIND == PH_AXPY)
+    if constexpr (KIND == PH_AXPY)
         epi_axpy<TI, FIRST, false>(md, t, pa, acc, row0, col0, lane, stg);
-    else if (KIND == PH_AXPY_LAST)
+    else if constexpr (KIND == PH_AXPY_LAST)
         epi_axpy<TI, FIRST, true>(md, t, pa, acc, row0, col0, lane, stg);
     else
         epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, stg);
+}
+
+// ---- AXPY with a master-seeded accumulator (swapped MFMA layout: lane holds
+// C[r][c..c+3] with r = row0 + 16 i + (lane & 15), c = col0 + 16 j + 4 (lane >> 4)).
+template <int TI, bool FIRST>
+__device__ __forceinline__ void axpy_init(const MatDesc& md, int row0, int col0, int lane, const PhaseArgs& pa,
+                                          f32x4_t (&acc)[TI][TI]) {
+    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+    if (!FIRST) {
+        const float* xm = reinterpret_cast<const float*>(pa.ws + md.off_xm);
+        const int64_t ld = md.Cp;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TI; ++j)   // padded buffer: always in bounds, zero outside R x C
+                acc[i][j] = *reinterpret_cast<const f32x4_t*>(xm + int64_t(row0 + 16 * i + l16) * ld + col0 + 16 * j + g4);
+    } else {
+        const bool nest = pa.nesterov != 0, vio = md.vec_io != 0;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TI; ++j) {
+                const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
+                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (r < md.R && c < md.C) {
+                    int nv = md.C - c;
+                    nv = nv > 4 ? 4 : nv;
+                    acc[i][j] = u4_at(md, r, c, pa.beta, nest, vio && nv == 4, nv);
+                }
+            }
+    }
+}
+
+template <int TI, bool FIRST, bool LAST>
+__device__ __forceinline__ void axpy_direct(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
+                                            const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane) {
+    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+    const float scale = pa.a * (FIRST ? pa.inv_norm[t.mat] : 1.f);
+    const int R = md.R, C = md.C;
+    if (!LAST) {
+        const int it = pa.iter;
+        float* xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
+        uint16_t* xb = reinterpret_cast<uint16_t*>(pa.ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
+        const int64_t ld = md.Cp;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TI; ++j) {
+                const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
+                if (r >= R || c >= C) continue;
+                const f32x4_t x = scale * acc[i][j];
+                const int64_t o = int64_t(r) * ld + c;
+                if (c + 4 <= C) {
+                    *reinterpret_cast<f32x4_t*>(xm + o) = x;
+                    st4_bf16(xb + o, x);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (c + q < C) {
+                            xm[o + q] = x[q];
+                            xb[o + q] = f32_to_bf16(x[q]);
+                        }
+                }
+            }
+        return;
+    }
+    // last iteration: W = W (1 - lr wd) - lr s O, and the optional fp32 O
+    const bool vio = md.vec_io != 0;
+    const float wdec = 1.f - pa.lr * pa.wd;
+    const float step = pa.lr * md.shape_scale;
+    f32x4_t wv[2][TI];
+    auto load_w = [&](int i, f32x4_t (&w)[TI]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < TI; ++j) {
+            const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
+            w[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (md.has_param && r < R && c < C) {
+                int nv = C - c;
+                nv = nv > 4 ? 4 : nv;
+                w[j] = ld4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vio && nv == 4, nv);
+            }
+        }
+    };
+    load_w(0, wv[0]);
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < TI) load_w(i + 1, wv[(i + 1) & 1]);   // one row block ahead
+#pragma unroll
+        for (int j = 0; j < TI; ++j) {
+            const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
+            if (r >= R || c >= C) continue;
+            int nv = C - c;
+            nv = nv > 4 ? 4 : nv;
+            const bool vec = vio && nv == 4;
+            const f32x4_t o = scale * acc[i][j];
+            if (md.has_param) {
+                f32x4_t w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = fmaf(-step, o[q], wv[i & 1][j][q] * wdec);
+                st4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vec, nv, w);
+            }
+            if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, o);
+        }
+    });
 }
 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
@@ -1052,18 +1166,37 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 #pragma unroll
         for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // operand layouts that occur: GRAM (kc, kc) or, for X0 = U^T, (ks, ks);
-    // POLY (kc, kc); AXPY (kc, ks) or, for X0 = U^T, (kc, kc)
-    if (KIND == PH_POLY || (op.a_kc && op.b_kc))
-        mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
-    else if (KIND == PH_GRAM)
-        mainloop<BM, kBK, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
-    else
-        mainloop<BM, kBK, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
-
-    __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-    epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
-                              reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
+    if constexpr ((KIND == PH_AXPY || KIND == PH_AXPY_LAST) && BM == 128) {
+        // accumulators start at the master X (loads issued before the operand
+        // loads, so their latency hides behind the pipeline fill); the MFMAs add
+        // (B / a) X and the epilogue only scales and stores
+        axpy_init<TI, FIRST>(md, row_a0 + wr, row_b0 + wc, lane, pa, acc);
+        if (op.a_kc && op.b_kc)
+            mainloop<BM, kBK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+        else
+            mainloop<BM, kBK, true, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+        axpy_direct<TI, FIRST, KIND == PH_AXPY_LAST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane);
+        return;
+    } else if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+        // 256-wide tiles: the accumulators fill all 256 AGPRs, so the master
+        // term is added in the LDS-staged epilogue instead
+        if (op.a_kc && op.b_kc)
+            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        else
+            mainloop<BM, kBK, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
+                                         reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
+    } else {
+        // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
+        if (KIND == PH_POLY || (op.a_kc && op.b_kc))
+            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        else
+            mainloop<BM, kBK, false, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
+                                         reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
+    }
 }
 
 // ---------------------------------------------------------------------------
