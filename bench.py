@@ -64,6 +64,79 @@ def algorithmic_work(wl):
     }
 
 
+KERNEL_SOURCES = ("newton_schulz_matrix_step_amd/csrc/muon_kernels.hip",
+                  "newton_schulz_matrix_step_amd/csrc/muon_api.cpp",
+                  "newton_schulz_matrix_step_amd/csrc/muon_internal.hpp")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel and planner sources: a recorded HBM-traffic figure
+    is reported only while the code it was measured on is unchanged."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def recorded_traffic(role: str, workload_name: str):
+    """HBM bytes per launch of ``role`` on ``workload_name`` from the counter
+    summary under profiles/ (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled
+    by the same counters' reading for a plain copy of known size), or None when
+    there is no summary or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{role}_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                rec[k.strip("`")] = v.strip().strip("`")
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return {"fetch": float(rec["fetch_bytes_per_launch"]), "write": float(rec["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_counters(paths):
+    """Mean per dispatch of every counter, per kernel, from rocprofv3
+    ``*_counter_collection.csv`` files (rows of one dispatch are summed)."""
+    import csv
+    from collections import defaultdict
+    tot = defaultdict(float)
+    disp = defaultdict(set)
+    for p in paths:
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                tot[key] += float(r["Counter_Value"])
+                disp[key].add(r["Dispatch_Id"])
+    rows = []
+    for (kname, cname), v in sorted(tot.items()):
+        nd = len(disp[(kname, cname)])
+        rows.append({"kernel": kname, "counter": cname, "dispatches": nd, "mean_per_dispatch": v / nd})
+    return rows
+
+
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain device-to-device copy of ``mib`` MiB, ``reps`` times: the known
+    byte count against which FETCH_SIZE / WRITE_SIZE readings are scaled."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
+
+
 def cpu_baseline(wl, grads_host, budget_s: float):
     """The oracle, as it stands, on the host cores: whole matrices of the first
     step until ``budget_s`` seconds of work, extrapolated to one full step."""
@@ -112,13 +185,26 @@ def main():
                     help="distinct seeded gradient sets resident in HBM (default: the workload's step count)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="only print per-kernel means of rocprofv3 counter CSV files and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        for r in summarize_counters(args.summarize_counters):
+            print(json.dumps(r))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
               "(every matrix's step is independent; the multi-GPU sharding is a design note, not code)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
 
     import torch
     import newton_schulz_matrix_step_amd as nsm
@@ -167,27 +253,31 @@ def main():
 
     work = algorithmic_work(wl)
 
-    # ---- timed region: plain handle, no per-kernel events ----
+    # ---- timed region: a profiling handle brackets every launch with HIP
+    # events on the launch stream, so the per-kernel durations come from the
+    # very steps that are timed ----
+    h = nsm.muon_init(0, nsm.MUON_INIT_PROFILE)
+    run_steps(h, args.warmup, 0)
+    torch.cuda.synchronize()
+    nsm.muon_kernel_stats_reset(h)
+    t0 = time.perf_counter()
+    run_steps(h, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = nsm.muon_kernel_stats_read(h)
+    ws_bytes = nsm.muon_workspace_bytes(h)
+    nsm.muon_destroy(h)
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- the same steps on a plain handle (no events), for comparison ----
     h = nsm.muon_init(0)
     run_steps(h, args.warmup, 0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run_steps(h, args.steps, args.warmup)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ws_bytes = nsm.muon_workspace_bytes(h)
+    plain_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     nsm.muon_destroy(h)
-    ms_per_step = elapsed * 1e3 / args.steps
-
-    # ---- per-kernel HIP-event timing: same steps on a profiling handle ----
-    hp_handle = nsm.muon_init(0, nsm.MUON_INIT_PROFILE)
-    run_steps(hp_handle, args.warmup, 0)
-    torch.cuda.synchronize()
-    nsm.muon_kernel_stats_reset(hp_handle)
-    run_steps(hp_handle, args.steps, args.warmup)
-    torch.cuda.synchronize()
-    stats = nsm.muon_kernel_stats_read(hp_handle)
-    nsm.muon_destroy(hp_handle)
 
     kernels = {}
     for name, (launches, total_ms) in stats.items():
@@ -214,6 +304,11 @@ def main():
         "frac": round(achieved / peak, 4),
         "traffic": None,
     }
+    tr = recorded_traffic(dom, wl.name)
+    if tr is not None:
+        roofline["traffic"] = round(tr["fetch"] + tr["write"])
+        roofline["traffic_fetch"] = round(tr["fetch"])
+        roofline["traffic_write"] = round(tr["write"])
     mom = kernels.get("momentum_norm", {})
 
     out = {
@@ -224,6 +319,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_no_events": round(plain_ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

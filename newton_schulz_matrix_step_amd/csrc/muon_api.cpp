@@ -354,16 +354,14 @@ hipEvent_t get_event(muon_handle* h) {
     return e;
 }
 
+// `launch(ev0, ev1)` enqueues one kernel; on a profiling handle the dispatch
+// records ev0 / ev1 at its start and end.
 template <class F>
-hipError_t timed(muon_handle* h, int role, hipStream_t s, F&& launch) {
-    if (!h->profile) return launch();
+hipError_t timed(muon_handle* h, int role, F&& launch) {
+    if (!h->profile) return launch(nullptr, nullptr);
     hipEvent_t a = get_event(h), b = get_event(h);
-    if (!a || !b) return launch();
-    hipError_t e = hipEventRecord(a, s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(b, s);
+    if (!a || !b) return launch(nullptr, nullptr);
+    const hipError_t e = launch(a, b);
     if (e == hipSuccess) h->pending.push_back(Pending{role, a, b});
     return e;
 }
@@ -433,10 +431,12 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
     ma.partials = plan.d_partials;
     ma.beta = hp->beta;
     ma.nesterov = hp->nesterov;
-    e = timed(h, K_MOMENTUM, stream, [&] { return launch_momentum(plan.d_units, plan.n_units, plan.d_desc, ma, f32c, stream); });
+    e = timed(h, K_MOMENTUM, [&](hipEvent_t e0, hipEvent_t e1) {
+        return launch_momentum(plan.d_units, plan.n_units, plan.d_desc, ma, f32c, stream, e0, e1);
+    });
     if (e != hipSuccess) return hip_fail(h, e, "momentum launch");
-    e = timed(h, K_FINALIZE, stream, [&] {
-        return launch_finalize_norm(plan.d_desc, n, plan.d_partials, plan.d_inv, plan.d_nu, hp->eps, stream);
+    e = timed(h, K_FINALIZE, [&](hipEvent_t e0, hipEvent_t e1) {
+        return launch_finalize_norm(plan.d_desc, n, plan.d_partials, plan.d_inv, plan.d_nu, hp->eps, stream, e0, e1);
     });
     if (e != hipSuccess) return hip_fail(h, e, "norm launch");
 
@@ -452,19 +452,26 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
     pa.nesterov = hp->nesterov;
     pa.iter = 0;
     if (hp->ns_steps == 0) {
-        e = timed(h, K_DIRECT, stream, [&] { return launch_direct_update(plan.d_units, plan.n_units, plan.d_desc, pa, stream); });
+        e = timed(h, K_DIRECT, [&](hipEvent_t e0, hipEvent_t e1) {
+            return launch_direct_update(plan.d_units, plan.n_units, plan.d_desc, pa, stream, e0, e1);
+        });
         if (e != hipSuccess) return hip_fail(h, e, "update launch");
         return MUON_OK;
     }
     for (int it = 1; it <= hp->ns_steps; ++it) {
         pa.iter = it;
-        e = timed(h, K_GRAM, stream, [&] { return launch_ns_phase(PH_GRAM, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        e = timed(h, K_GRAM, [&](hipEvent_t e0, hipEvent_t e1) {
+            return launch_ns_phase(PH_GRAM, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream, e0, e1);
+        });
         if (e != hipSuccess) return hip_fail(h, e, "gram launch");
-        e = timed(h, K_POLY, stream, [&] { return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream); });
+        e = timed(h, K_POLY, [&](hipEvent_t e0, hipEvent_t e1) {
+            return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream, e0, e1);
+        });
         if (e != hipSuccess) return hip_fail(h, e, "poly launch");
         const bool last = it == hp->ns_steps;
-        e = timed(h, last ? K_AXPY_LAST : K_AXPY, stream, [&] {
-            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.axpy_tile, plan.d_axpy, plan.n_axpy, plan.d_desc, pa, stream);
+        e = timed(h, last ? K_AXPY_LAST : K_AXPY, [&](hipEvent_t e0, hipEvent_t e1) {
+            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.axpy_tile, plan.d_axpy, plan.n_axpy,
+                                   plan.d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "axpy launch");
     }

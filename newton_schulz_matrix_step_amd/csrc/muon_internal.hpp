@@ -68,16 +68,20 @@ struct MomentumArgs {
     int32_t nesterov;
 };
 
-// Launch wrappers (muon_kernels.hip).  All return the launch status.
+// Launch wrappers (muon_kernels.hip).  All return the launch status.  ev0 / ev1,
+// when not null, are recorded by the dispatch itself at the kernel's start and
+// end (hipExtLaunchKernelGGL), which adds no packets to the stream.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a,
-                           bool f32_compute, hipStream_t s);
+                           bool f32_compute, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials,
-                                float* inv_norm, float* nu, float eps, hipStream_t s);
+                                float* inv_norm, float* nu, float eps, hipStream_t s,
+                                hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* tiles, int n_tiles,
-                           const MatDesc* mats, PhaseArgs a, hipStream_t s);
+                           const MatDesc* mats, PhaseArgs a, hipStream_t s,
+                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats,
-                                PhaseArgs a, hipStream_t s);
+                                PhaseArgs a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Tile edges of the Newton-Schulz GEMMs: fp32 mode uses kTileF32; bf16 mode
 // picks kTileLarge or kTileSmall per phase from the tile count.

@@ -20,6 +20,8 @@
 // as [row][k] in 16-byte chunks, XOR-swizzled; an operand whose k index is the
 // row index in memory is transposed in registers on its way to LDS.
 
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "muon_internal.hpp"
@@ -32,6 +34,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+
+// Every buffer the kernels read or write outside LDS (caller tensors, workspace)
+// is global memory.  Pointers loaded from a descriptor are generic, and generic
+// accesses become flat instructions, which count against the LDS wait counter as
+// well: an epilogue that mixes them with LDS staging waits for its global loads
+// at every LDS wait.  gm() restates the address space.
+#define GMEM __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ GMEM T* gm(T* p) { return (GMEM T*)p; }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -47,14 +58,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // dtype 0 = bf16, 1 = f32
 __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
-    return dt == 0 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+    return dt == 0 ? bf16_to_f32(gm(static_cast<const uint16_t*>(p))[i]) : gm(static_cast<const float*>(p))[i];
 }
 
 __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float v) {
     if (dt == 0)
-        static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+        gm(static_cast<uint16_t*>(p))[i] = f32_to_bf16(v);
     else
-        static_cast<float*>(p)[i] = v;
+        gm(static_cast<float*>(p))[i] = v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -79,7 +90,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 __device__ __forceinline__ float u_at(const MatDesc& md, int64_t r, int64_t c, float beta, bool nest) {
     const float g = load_elem(md.grad, r * md.ld_grad + c, md.io_dtype);
     if (!md.has_mom) return g;
-    const float mn = md.mom[r * md.ld_mom + c];
+    const float mn = gm(md.mom)[r * md.ld_mom + c];
     return nest ? fmaf(beta, mn, g) : mn;
 }
 
@@ -118,21 +129,21 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
             const int64_t r = un.r0 + rr;
             float g[8];
             if (md.io_dtype == 0) {
-                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(md.grad) + r * md.ld_grad + c);
+                const u32x4_t v = *gm(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(md.grad) + r * md.ld_grad + c));
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     g[2 * q] = __uint_as_float(v[q] << 16);
                     g[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
                 }
             } else {
-                const f32x4_t* gp = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(md.grad) + r * md.ld_grad + c);
+                const GMEM f32x4_t* gp = gm(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(md.grad) + r * md.ld_grad + c));
                 const f32x4_t v0 = gp[0], v1 = gp[1];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) { g[q] = v0[q]; g[4 + q] = v1[q]; }
             }
             float u[8];
             if (has_mom) {
-                f32x4_t* mp = reinterpret_cast<f32x4_t*>(md.mom + r * md.ld_mom + c);
+                GMEM f32x4_t* mp = gm(reinterpret_cast<f32x4_t*>(md.mom + r * md.ld_mom + c));
                 f32x4_t m0 = mp[0], m1 = mp[1];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -153,14 +164,14 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
 #pragma unroll
             for (int q = 0; q < 8; ++q) ss = fmaf(u[q], u[q], ss);
             if (F32C) {
-                f32x4_t* up = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + r * ldu + c);
+                GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + r * ldu + c));
                 up[0] = f32x4_t{u[0], u[1], u[2], u[3]};
                 up[1] = f32x4_t{u[4], u[5], u[6], u[7]};
             } else {
                 u32x4_t w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(u[2 * q], u[2 * q + 1]);
-                *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + r * ldu + c) = w;
+                *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + r * ldu + c)) = w;
             }
         }
     } else {
@@ -172,16 +183,16 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
             const float g = load_elem(md.grad, r * md.ld_grad + c, md.io_dtype);
             float u = g;
             if (has_mom) {
-                float* mp = md.mom + r * md.ld_mom + c;
+                GMEM float* mp = gm(md.mom + r * md.ld_mom + c);
                 const float mn = fmaf(beta, *mp, g);
                 *mp = mn;
                 u = nest ? fmaf(beta, mn, g) : mn;
             }
             ss = fmaf(u, u, ss);
             if (F32C)
-                reinterpret_cast<float*>(ub)[r * ldu + c] = u;
+                gm(reinterpret_cast<float*>(ub))[r * ldu + c] = u;
             else
-                reinterpret_cast<uint16_t*>(ub)[r * ldu + c] = f32_to_bf16(u);
+                gm(reinterpret_cast<uint16_t*>(ub))[r * ldu + c] = f32_to_bf16(u);
         }
     }
     const float tot = block_sum(ss, red);
@@ -436,7 +447,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
                                 const float w = load_elem(md.param, pi, md.io_dtype);
                                 store_elem(md.param, pi, md.io_dtype, fmaf(-step, v, w * wdec));
                             }
-                            if (md.upd) md.upd[int64_t(r) * md.ld_upd + c] = v;
+                            if (md.upd) gm(md.upd)[int64_t(r) * md.ld_upd + c] = v;
                         }
                     }
                 }
@@ -716,18 +727,18 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t ld4_bf16(const void* p) {
-    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t w = *gm(reinterpret_cast<const u32x2_t*>(p));
     return f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
                    __uint_as_float(w[1] & 0xFFFF0000u)};
 }
 __device__ __forceinline__ void st4_bf16(void* p, f32x4_t v) {
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *gm(reinterpret_cast<u32x2_t*>(p)) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 // 4 consecutive elements of a caller buffer (dtype 0 bf16 / 1 f32); `vec`: aligned and in range
 __device__ __forceinline__ f32x4_t ld4_io(const void* p, int64_t i, int dt, bool vec, int nvalid) {
     if (vec) {
         if (dt == 0) return ld4_bf16(static_cast<const uint16_t*>(p) + i);
-        return *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+        return *gm(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i));
     }
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -740,7 +751,7 @@ __device__ __forceinline__ void st4_io(void* p, int64_t i, int dt, bool vec, int
         if (dt == 0)
             st4_bf16(static_cast<uint16_t*>(p) + i, v);
         else
-            *reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i) = v;
+            *gm(reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i)) = v;
         return;
     }
 #pragma unroll
@@ -748,13 +759,45 @@ __device__ __forceinline__ void st4_io(void* p, int64_t i, int dt, bool vec, int
         if (q < nvalid) store_elem(p, i + q, dt, v[q]);
 }
 
-// u at 4 consecutive stored elements (r, c..c+3)
-__device__ __forceinline__ f32x4_t u4_at(const MatDesc& md, int64_t r, int64_t c, float beta, bool nest, bool vec,
-                                         int nvalid) {
-    const f32x4_t g = ld4_io(md.grad, r * md.ld_grad + c, md.io_dtype, vec, nvalid);
-    if (!md.has_mom) return g;
-    const f32x4_t mn = ld4_io(md.mom, r * md.ld_mom + c, 1, vec, nvalid);
-    if (!nest) return mn;
+// The caller-buffer fields of one descriptor, copied into registers once per
+// epilogue: read through the descriptor after the epilogue's own global stores,
+// they would be reloaded (the compiler cannot rule out that a store hit the
+// descriptor table), each reload costing a full wait on outstanding memory.
+struct IoView {
+    const void* grad;
+    const float* mom;
+    void* param;
+    float* upd;
+    int64_t ld_grad, ld_mom, ld_param, ld_upd;
+    int dt;                     // storage dtype of param / grad
+    bool has_mom, has_param, nest, vio;
+};
+
+__device__ __forceinline__ IoView io_view(const MatDesc& md, bool nest) {
+    IoView v;
+    v.grad = md.grad;
+    v.mom = md.mom;
+    v.param = md.param;
+    v.upd = md.upd;
+    v.ld_grad = md.ld_grad;
+    v.ld_mom = md.ld_mom;
+    v.ld_param = md.ld_param;
+    v.ld_upd = md.ld_upd;
+    v.dt = md.io_dtype;
+    v.has_mom = md.has_mom != 0;
+    v.has_param = md.has_param != 0;
+    v.nest = nest;
+    v.vio = md.vec_io != 0;
+    return v;
+}
+
+// u at 4 consecutive stored elements (r, c..c+3): m' (or g without momentum),
+// g + beta m' with Nesterov; only the buffers the form needs are read
+__device__ __forceinline__ f32x4_t u4_at(const IoView& v, int64_t r, int64_t c, float beta, bool vec, int nvalid) {
+    if (!v.has_mom) return ld4_io(v.grad, r * v.ld_grad + c, v.dt, vec, nvalid);
+    const f32x4_t mn = ld4_io(v.mom, r * v.ld_mom + c, 1, vec, nvalid);
+    if (!v.nest) return mn;
+    const f32x4_t g = ld4_io(v.grad, r * v.ld_grad + c, v.dt, vec, nvalid);
     f32x4_t u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) u[q] = fmaf(beta, mn[q], g[q]);
@@ -812,86 +855,165 @@ struct AxpyCtx {
     uint16_t* xb_next;
     int64_t ldq;
     int R, C;
-    bool nest, vio;
+    bool vio;
     float alpha, a, beta, wdec, step;
+    IoView io;
 };
 
-template <int TI, bool FIRST, bool LAST>
-__device__ __forceinline__ void axpy_load(const MatDesc& md, const AxpyCtx& x, int row0, int col0, int lane, int band,
-                                          f32x4_t (&mst)[EpiGeom<TI>::NQ], f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
+// 4 consecutive elements of a caller buffer exactly as loaded (f32: 4 words;
+// bf16: 2 words in [0], [1]).  Decoding happens where the values are used, so
+// the wait for a load falls at its use, a band later, not right after issue.
+__device__ __forceinline__ u32x4_t ld4_raw(const void* p, int64_t i, int dt, bool vec, int nvalid) {
+    u32x4_t r = {0u, 0u, 0u, 0u};
+    if (vec) {
+        if (dt == 0) {
+            const u32x2_t w = *gm(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p) + i));
+            r[0] = w[0];
+            r[1] = w[1];
+        } else {
+            r = *gm(reinterpret_cast<const u32x4_t*>(static_cast<const float*>(p) + i));
+        }
+        return r;
+    }
+    if (dt == 0) {
+        const GMEM uint16_t* q = gm(static_cast<const uint16_t*>(p)) + i;
+        uint32_t h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < nvalid) h[k] = q[k];
+        r[0] = h[0] | (h[1] << 16);
+        r[1] = h[2] | (h[3] << 16);
+    } else {
+        const GMEM uint32_t* q = gm(static_cast<const uint32_t*>(p)) + i;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < nvalid) r[k] = q[k];
+    }
+    return r;
+}
+
+__device__ __forceinline__ f32x4_t dec4(u32x4_t r, int dt) {
+    if (dt == 0)
+        return f32x4_t{__uint_as_float(r[0] << 16), __uint_as_float(r[0] & 0xFFFF0000u),
+                       __uint_as_float(r[1] << 16), __uint_as_float(r[1] & 0xFFFF0000u)};
+    return f32x4_t{__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2]), __uint_as_float(r[3])};
+}
+
+// Raw operands of one band of the AXPY epilogue, per 4-element run:
+//   ra: the master (workspace fp32) or, on the first iteration, m' (g without
+//       a momentum buffer);  rb: g on the first iteration with Nesterov;
+//   rc: W on the last iteration.
+template <int TI>
+struct AxpyRaw {
+    u32x4_t ra[EpiGeom<TI>::NQ], rb[EpiGeom<TI>::NQ], rc[EpiGeom<TI>::NQ];
+};
+
+// EDGE = false: the wave's whole tile lies inside R x C and every caller buffer
+// allows 4-element vectors, so no access needs a bounds check or a scalar tail.
+template <int TI, bool FIRST, bool LAST, bool EDGE>
+__device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, int lane, int band, AxpyRaw<TI>& w) {
 #pragma unroll
     for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
         int lr, lc;
         row_run<TI>(q, lane, lr, lc);
         const int r = row0 + 16 * band + lr, c = col0 + lc;
+        int nv = x.C - c;
+        nv = nv > 4 ? 4 : nv;
+        const bool in = !EDGE || (r < x.R && c < x.C);
+        const bool vec = !EDGE || (x.vio && nv == 4);
         if (!FIRST) {
-            mst[q] = *reinterpret_cast<const f32x4_t*>(x.xm + int64_t(r) * x.ldq + c);   // padded: in bounds
+            w.ra[q] = *gm(reinterpret_cast<const u32x4_t*>(x.xm + int64_t(r) * x.ldq + c));   // padded: in bounds
         } else {
-            mst[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (r < x.R && c < x.C) {
-                int nv = x.C - c;
-                nv = nv > 4 ? 4 : nv;
-                mst[q] = u4_at(md, r, c, x.beta, x.nest, x.vio && nv == 4, nv);
+            w.ra[q] = u32x4_t{0u, 0u, 0u, 0u};
+            w.rb[q] = u32x4_t{0u, 0u, 0u, 0u};
+            if (in) {
+                if (x.io.has_mom) {
+                    w.ra[q] = ld4_raw(x.io.mom, int64_t(r) * x.io.ld_mom + c, 1, vec, nv);
+                    if (x.io.nest) w.rb[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, x.io.dt, vec, nv);
+                } else {
+                    w.ra[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, x.io.dt, vec, nv);
+                }
             }
         }
         if (LAST) {
-            wv[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (md.has_param && r < x.R && c < x.C) {
-                int nv = x.C - c;
-                nv = nv > 4 ? 4 : nv;
-                wv[q] = ld4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, x.vio && nv == 4, nv);
-            }
+            w.rc[q] = u32x4_t{0u, 0u, 0u, 0u};
+            if (x.io.has_param && in) w.rc[q] = ld4_raw(x.io.param, int64_t(r) * x.io.ld_param + c, x.io.dt, vec, nv);
         }
     }
 }
 
-template <int TI, bool LAST>
-__device__ __forceinline__ void axpy_store(const MatDesc& md, const AxpyCtx& x, const float* __restrict__ stg,
-                                           int row0, int col0, int lane, int band,
-                                           const f32x4_t (&mst)[EpiGeom<TI>::NQ],
-                                           const f32x4_t (&wv)[EpiGeom<TI>::NQ]) {
+template <int TI, bool FIRST, bool LAST, bool EDGE>
+__device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
+                                           int lane, int band, const AxpyRaw<TI>& w) {
     using E = EpiGeom<TI>;
 #pragma unroll
     for (int q = 0; q < E::NQ; ++q) {
         int lr, lc;
         row_run<TI>(q, lane, lr, lc);
         const int r = row0 + 16 * band + lr, c = col0 + lc;
-        if (r >= x.R || c >= x.C) continue;
+        if (EDGE && (r >= x.R || c >= x.C)) continue;
         int nv = x.C - c;
         nv = nv > 4 ? 4 : nv;
+        f32x4_t mst;
+        if (!FIRST) {
+            mst = dec4(w.ra[q], 1);
+        } else if (x.io.has_mom) {
+            mst = dec4(w.ra[q], 1);
+            if (x.io.nest) {
+                const f32x4_t g = dec4(w.rb[q], x.io.dt);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) mst[k] = fmaf(x.beta, mst[k], g[k]);
+            }
+        } else {
+            mst = dec4(w.ra[q], x.io.dt);
+        }
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
-        const f32x4_t o = x.alpha * (x.a * (mst[q] + v));   // acc holds (B / a) X
+        const f32x4_t o = x.alpha * (x.a * (mst + v));   // acc holds (B / a) X
         if (!LAST) {
             const int64_t off = int64_t(r) * x.ldq + c;
-            if (nv == 4) {
-                *reinterpret_cast<f32x4_t*>(x.xm + off) = o;
+            if (!EDGE || nv == 4) {
+                *gm(reinterpret_cast<f32x4_t*>(x.xm + off)) = o;
                 st4_bf16(x.xb_next + off, o);
             } else {
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
                     if (q2 < nv) {
-                        x.xm[off + q2] = o[q2];
-                        x.xb_next[off + q2] = f32_to_bf16(o[q2]);
+                        gm(x.xm)[off + q2] = o[q2];
+                        gm(x.xb_next)[off + q2] = f32_to_bf16(o[q2]);
                     }
             }
         } else {
-            const bool vec = x.vio && nv == 4;
-            if (md.has_param) {
-                f32x4_t w;
+            const bool vec = !EDGE || (x.vio && nv == 4);
+            if (x.io.has_param) {
+                const f32x4_t wold = dec4(w.rc[q], x.io.dt);
+                f32x4_t wn;
 #pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) w[q2] = fmaf(-x.step, o[q2], wv[q][q2] * x.wdec);
-                st4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vec, nv, w);
+                for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-x.step, o[q2], wold[q2] * x.wdec);
+                st4_io(x.io.param, int64_t(r) * x.io.ld_param + c, x.io.dt, vec, nv, wn);
             }
-            if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, o);
+            if (x.io.upd) st4_io(x.io.upd, int64_t(r) * x.io.ld_upd + c, 1, vec, nv, o);
         }
     }
+}
+
+template <int TI, bool FIRST, bool LAST, bool EDGE>
+__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const f32x4_t (&acc)[TI][TI], int row0, int col0,
+                                              int lane, float* __restrict__ stg) {
+    AxpyRaw<TI> w[2];
+    axpy_load<TI, FIRST, LAST, EDGE>(x, row0, col0, lane, 0, w[0]);
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + 1 < TI)   // one band ahead
+            axpy_load<TI, FIRST, LAST, EDGE>(x, row0, col0, lane, i + 1, w[(i + 1) & 1]);
+        stage_band<TI>(stg, acc, i, lane);
+        axpy_store<TI, FIRST, LAST, EDGE>(x, stg, row0, col0, lane, i, w[i & 1]);
+    });
 }
 
 template <int TI, bool FIRST, bool LAST>
 __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                          const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                          float* __restrict__ stg) {
-    constexpr int NQ = EpiGeom<TI>::NQ;
     AxpyCtx x;
     const int it = pa.iter;
     x.xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
@@ -899,22 +1021,18 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
     x.ldq = md.Cp;
     x.R = md.R;
     x.C = md.C;
-    x.nest = pa.nesterov != 0;
     x.vio = md.vec_io != 0;
     x.alpha = FIRST ? pa.inv_norm[t.mat] : 1.f;
     x.a = pa.a;
     x.beta = pa.beta;
     x.wdec = 1.f - pa.lr * pa.wd;
     x.step = pa.lr * md.shape_scale;
-    f32x4_t mst[2][NQ], wv[2][NQ];
-    axpy_load<TI, FIRST, LAST>(md, x, row0, col0, lane, 0, mst[0], wv[0]);
-    static_for<0, TI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + 1 < TI)   // one band ahead
-            axpy_load<TI, FIRST, LAST>(md, x, row0, col0, lane, i + 1, mst[(i + 1) & 1], wv[(i + 1) & 1]);
-        stage_band<TI>(stg, acc, i, lane);
-        axpy_store<TI, LAST>(md, x, stg, row0, col0, lane, i, mst[i & 1], wv[i & 1]);
-    });
+    x.io = io_view(md, pa.nesterov != 0);
+    constexpr int WT = EpiGeom<TI>::WT;
+    if (x.vio && row0 + WT <= x.R && col0 + WT <= x.C)
+        epi_axpy_body<TI, FIRST, LAST, false>(x, acc, row0, col0, lane, stg);
+    else
+        epi_axpy_body<TI, FIRST, LAST, true>(x, acc, row0, col0, lane, stg);
 }
 
 // ---- GRAM (A = s^2 X X^T) and POLY (B / a = (b A + c A A) / a): upper triangle written
@@ -1052,17 +1170,18 @@ __device__ __forceinline__ void axpy_init(const MatDesc& md, int row0, int col0,
             for (int j = 0; j < TI; ++j)   // padded buffer: always in bounds, zero outside R x C
                 acc[i][j] = *reinterpret_cast<const f32x4_t*>(xm + int64_t(row0 + 16 * i + l16) * ld + col0 + 16 * j + g4);
     } else {
-        const bool nest = pa.nesterov != 0, vio = md.vec_io != 0;
+        const IoView io = io_view(md, pa.nesterov != 0);
+        const int R = md.R, C = md.C;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int j = 0; j < TI; ++j) {
                 const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
                 acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (r < md.R && c < md.C) {
-                    int nv = md.C - c;
+                if (r < R && c < C) {
+                    int nv = C - c;
                     nv = nv > 4 ? 4 : nv;
-                    acc[i][j] = u4_at(md, r, c, pa.beta, nest, vio && nv == 4, nv);
+                    acc[i][j] = u4_at(io, r, c, pa.beta, io.vio && nv == 4, nv);
                 }
             }
     }
@@ -1102,7 +1221,8 @@ __device__ __forceinline__ void axpy_direct(const MatDesc& md, const Tile& t, co
         return;
     }
     // last iteration: W = W (1 - lr wd) - lr s O, and the optional fp32 O
-    const bool vio = md.vec_io != 0;
+    const IoView io = io_view(md, false);
+    const bool vio = io.vio;
     const float wdec = 1.f - pa.lr * pa.wd;
     const float step = pa.lr * md.shape_scale;
     f32x4_t wv[2][TI];
@@ -1111,10 +1231,10 @@ __device__ __forceinline__ void axpy_direct(const MatDesc& md, const Tile& t, co
         for (int j = 0; j < TI; ++j) {
             const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
             w[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (md.has_param && r < R && c < C) {
+            if (io.has_param && r < R && c < C) {
                 int nv = C - c;
                 nv = nv > 4 ? 4 : nv;
-                w[j] = ld4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vio && nv == 4, nv);
+                w[j] = ld4_io(io.param, int64_t(r) * io.ld_param + c, io.dt, vio && nv == 4, nv);
             }
         }
     };
@@ -1130,13 +1250,13 @@ __device__ __forceinline__ void axpy_direct(const MatDesc& md, const Tile& t, co
             nv = nv > 4 ? 4 : nv;
             const bool vec = vio && nv == 4;
             const f32x4_t o = scale * acc[i][j];
-            if (md.has_param) {
+            if (io.has_param) {
                 f32x4_t w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = fmaf(-step, o[q], wv[i & 1][j][q] * wdec);
-                st4_io(md.param, int64_t(r) * md.ld_param + c, md.io_dtype, vec, nv, w);
+                st4_io(io.param, int64_t(r) * io.ld_param + c, io.dt, vec, nv, w);
             }
-            if (md.upd) st4_io(md.upd, int64_t(r) * md.ld_upd + c, 1, vec, nv, o);
+            if (io.upd) st4_io(io.upd, int64_t(r) * io.ld_upd + c, 1, vec, nv, o);
         }
     });
 }
@@ -1221,7 +1341,7 @@ __global__ __launch_bounds__(kThreads) void direct_update_kernel(const Unit* __r
             const float w = load_elem(md.param, pi, md.io_dtype);
             store_elem(md.param, pi, md.io_dtype, fmaf(-step, o, w * wdec));
         }
-        if (md.upd) md.upd[r * md.ld_upd + c] = o;
+        if (md.upd) gm(md.upd)[r * md.ld_upd + c] = o;
     }
 }
 
@@ -1240,63 +1360,68 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a, bool f32c,
-                           hipStream_t s) {
+                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_units <= 0) return hipSuccess;
     if (f32c)
-        hipLaunchKernelGGL(momentum_kernel<true>, dim3(n_units), dim3(kThreads), 0, s, units, mats, a);
+        hipExtLaunchKernelGGL(momentum_kernel<true>, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
     else
-        hipLaunchKernelGGL(momentum_kernel<false>, dim3(n_units), dim3(kThreads), 0, s, units, mats, a);
+        hipExtLaunchKernelGGL(momentum_kernel<false>, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
     return hipGetLastError();
 }
 
 hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials, float* inv_norm, float* nu,
-                                float eps, hipStream_t s) {
+                                float eps, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_mats <= 0) return hipSuccess;
-    hipLaunchKernelGGL(finalize_norm_kernel, dim3(n_mats), dim3(kThreads), 0, s, mats, partials, inv_norm, nu, eps);
+    hipExtLaunchKernelGGL(finalize_norm_kernel, dim3(n_mats), dim3(kThreads), 0, s, ev0, ev1, 0, mats, partials,
+                          inv_norm, nu, eps);
     return hipGetLastError();
 }
 
 template <int KIND, int BM>
-static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s) {
+static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s,
+                        hipEvent_t ev0, hipEvent_t ev1) {
     // only AXPY epilogues differ on the first iteration
     if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
         if (first) {
-            hipLaunchKernelGGL((ns_gemm_bf16<KIND, BM, true>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a,
-                               n_tiles);
+            hipExtLaunchKernelGGL((ns_gemm_bf16<KIND, BM, true>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0,
+                                  tiles, mats, a, n_tiles);
             return;
         }
     }
-    hipLaunchKernelGGL((ns_gemm_bf16<KIND, BM, false>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a, n_tiles);
+    hipExtLaunchKernelGGL((ns_gemm_bf16<KIND, BM, false>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0, tiles,
+                          mats, a, n_tiles);
 }
 
 template <int KIND>
 static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
-                        hipStream_t s) {
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (f32c)
-        hipLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, tiles, mats, a);
+        hipExtLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0, tiles,
+                              mats, a);
     else if (tile == 256)
-        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s);
+        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
     else
-        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s);
+        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
-                           PhaseArgs a, hipStream_t s) {
+                           PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
     if (f32c ? tile != 128 : (tile != 128 && tile != 256)) return hipErrorInvalidValue;
     switch (kind) {
-        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s); break;
-        case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s); break;
-        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tile, tiles, n_tiles, mats, a, s); break;
-        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tile, tiles, n_tiles, mats, a, s); break;
+        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats, PhaseArgs a, hipStream_t s) {
+hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats, PhaseArgs a, hipStream_t s,
+                                hipEvent_t ev0, hipEvent_t ev1) {
     if (n_units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(direct_update_kernel, dim3(n_units), dim3(kThreads), 0, s, units, mats, a);
+    hipExtLaunchKernelGGL(direct_update_kernel, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
     return hipGetLastError();
 }
 
