@@ -837,15 +837,6 @@ __device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
     lr = idx / WT;
     lc = idx % WT;
 }
-// Column-major pass geometry: run q of a lane covers band rows 4 quad..+3 of column lc.
-template <int TI>
-__device__ __forceinline__ void col_run(int q, int lane, int& quad, int& lc) {
-    constexpr int WT = EpiGeom<TI>::WT;
-    const int task = q * 64 + lane;
-    lc = task % WT;
-    quad = task / WT;
-}
-
 // ---- AXPY: X' = alpha (a X + B X) on the stored R x C tile grid (see
 // resolve_operands): fp32 master and bf16 operand copy, or on the last
 // iteration O = X' applied to the weight: W = W (1 - lr wd) - lr s O and the
@@ -899,6 +890,31 @@ __device__ __forceinline__ f32x4_t dec4(u32x4_t r, int dt) {
     return f32x4_t{__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[2]), __uint_as_float(r[3])};
 }
 
+// Caller-buffer configuration of an AXPY epilogue: read from the descriptor at
+// run time (IoRuntime), or fixed at compile time (IoFixed) for the interior
+// fast path, where it removes every per-run branch on dtype and buffer presence.
+struct IoRuntime {
+    static constexpr bool fixed = false;
+    static constexpr int dt = 0;
+    static constexpr bool mom = false, nest = false, param = false, upd = false;
+};
+template <int DT, bool MOM, bool NEST, bool PARAM, bool UPD>
+struct IoFixed {
+    static constexpr bool fixed = true;
+    static constexpr int dt = DT;
+    static constexpr bool mom = MOM, nest = NEST, param = PARAM, upd = UPD;
+};
+template <class M>
+__device__ __forceinline__ int io_dt(const IoView& v) { if constexpr (M::fixed) return M::dt; else return v.dt; }
+template <class M>
+__device__ __forceinline__ bool io_mom(const IoView& v) { if constexpr (M::fixed) return M::mom; else return v.has_mom; }
+template <class M>
+__device__ __forceinline__ bool io_nest(const IoView& v) { if constexpr (M::fixed) return M::nest; else return v.nest; }
+template <class M>
+__device__ __forceinline__ bool io_param(const IoView& v) { if constexpr (M::fixed) return M::param; else return v.has_param; }
+template <class M>
+__device__ __forceinline__ bool io_upd(const IoView& v) { if constexpr (M::fixed) return M::upd; else return v.upd != nullptr; }
+
 // Raw operands of one band of the AXPY epilogue, per 4-element run:
 //   ra: the master (workspace fp32) or, on the first iteration, m' (g without
 //       a momentum buffer);  rb: g on the first iteration with Nesterov;
@@ -910,7 +926,7 @@ struct AxpyRaw {
 
 // EDGE = false: the wave's whole tile lies inside R x C and every caller buffer
 // allows 4-element vectors, so no access needs a bounds check or a scalar tail.
-template <int TI, bool FIRST, bool LAST, bool EDGE>
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M>
 __device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, int lane, int band, AxpyRaw<TI>& w) {
 #pragma unroll
     for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
@@ -927,22 +943,24 @@ __device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, 
             w.ra[q] = u32x4_t{0u, 0u, 0u, 0u};
             w.rb[q] = u32x4_t{0u, 0u, 0u, 0u};
             if (in) {
-                if (x.io.has_mom) {
+                if (io_mom<M>(x.io)) {
                     w.ra[q] = ld4_raw(x.io.mom, int64_t(r) * x.io.ld_mom + c, 1, vec, nv);
-                    if (x.io.nest) w.rb[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, x.io.dt, vec, nv);
+                    if (io_nest<M>(x.io))
+                        w.rb[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, io_dt<M>(x.io), vec, nv);
                 } else {
-                    w.ra[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, x.io.dt, vec, nv);
+                    w.ra[q] = ld4_raw(x.io.grad, int64_t(r) * x.io.ld_grad + c, io_dt<M>(x.io), vec, nv);
                 }
             }
         }
         if (LAST) {
             w.rc[q] = u32x4_t{0u, 0u, 0u, 0u};
-            if (x.io.has_param && in) w.rc[q] = ld4_raw(x.io.param, int64_t(r) * x.io.ld_param + c, x.io.dt, vec, nv);
+            if (io_param<M>(x.io) && in)
+                w.rc[q] = ld4_raw(x.io.param, int64_t(r) * x.io.ld_param + c, io_dt<M>(x.io), vec, nv);
         }
     }
 }
 
-template <int TI, bool FIRST, bool LAST, bool EDGE>
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M>
 __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __restrict__ stg, int row0, int col0,
                                            int lane, int band, const AxpyRaw<TI>& w) {
     using E = EpiGeom<TI>;
@@ -957,15 +975,15 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         f32x4_t mst;
         if (!FIRST) {
             mst = dec4(w.ra[q], 1);
-        } else if (x.io.has_mom) {
+        } else if (io_mom<M>(x.io)) {
             mst = dec4(w.ra[q], 1);
-            if (x.io.nest) {
-                const f32x4_t g = dec4(w.rb[q], x.io.dt);
+            if (io_nest<M>(x.io)) {
+                const f32x4_t g = dec4(w.rb[q], io_dt<M>(x.io));
 #pragma unroll
                 for (int k = 0; k < 4; ++k) mst[k] = fmaf(x.beta, mst[k], g[k]);
             }
         } else {
-            mst = dec4(w.ra[q], x.io.dt);
+            mst = dec4(w.ra[q], io_dt<M>(x.io));
         }
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
         const f32x4_t o = x.alpha * (x.a * (mst + v));   // acc holds (B / a) X
@@ -984,29 +1002,29 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
             }
         } else {
             const bool vec = !EDGE || (x.vio && nv == 4);
-            if (x.io.has_param) {
-                const f32x4_t wold = dec4(w.rc[q], x.io.dt);
+            if (io_param<M>(x.io)) {
+                const f32x4_t wold = dec4(w.rc[q], io_dt<M>(x.io));
                 f32x4_t wn;
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) wn[q2] = fmaf(-x.step, o[q2], wold[q2] * x.wdec);
-                st4_io(x.io.param, int64_t(r) * x.io.ld_param + c, x.io.dt, vec, nv, wn);
+                st4_io(x.io.param, int64_t(r) * x.io.ld_param + c, io_dt<M>(x.io), vec, nv, wn);
             }
-            if (x.io.upd) st4_io(x.io.upd, int64_t(r) * x.io.ld_upd + c, 1, vec, nv, o);
+            if (io_upd<M>(x.io)) st4_io(x.io.upd, int64_t(r) * x.io.ld_upd + c, 1, vec, nv, o);
         }
     }
 }
 
-template <int TI, bool FIRST, bool LAST, bool EDGE>
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M>
 __device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const f32x4_t (&acc)[TI][TI], int row0, int col0,
                                               int lane, float* __restrict__ stg) {
     AxpyRaw<TI> w[2];
-    axpy_load<TI, FIRST, LAST, EDGE>(x, row0, col0, lane, 0, w[0]);
+    axpy_load<TI, FIRST, LAST, EDGE, M>(x, row0, col0, lane, 0, w[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i + 1 < TI)   // one band ahead
-            axpy_load<TI, FIRST, LAST, EDGE>(x, row0, col0, lane, i + 1, w[(i + 1) & 1]);
+            axpy_load<TI, FIRST, LAST, EDGE, M>(x, row0, col0, lane, i + 1, w[(i + 1) & 1]);
         stage_band<TI>(stg, acc, i, lane);
-        axpy_store<TI, FIRST, LAST, EDGE>(x, stg, row0, col0, lane, i, w[i & 1]);
+        axpy_store<TI, FIRST, LAST, EDGE, M>(x, stg, row0, col0, lane, i, w[i & 1]);
     });
 }
 
@@ -1029,100 +1047,176 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
     x.step = pa.lr * md.shape_scale;
     x.io = io_view(md, pa.nesterov != 0);
     constexpr int WT = EpiGeom<TI>::WT;
-    if (x.vio && row0 + WT <= x.R && col0 + WT <= x.C)
-        epi_axpy_body<TI, FIRST, LAST, false>(x, acc, row0, col0, lane, stg);
-    else
-        epi_axpy_body<TI, FIRST, LAST, true>(x, acc, row0, col0, lane, stg);
+    if (!(x.vio && row0 + WT <= x.R && col0 + WT <= x.C)) {
+        epi_axpy_body<TI, FIRST, LAST, true, IoRuntime>(x, acc, row0, col0, lane, stg);
+        return;
+    }
+    // interior: pick the caller-buffer configuration at compile time
+    const IoView& v = x.io;
+    if constexpr (FIRST == LAST) {   // middle iterations read no caller buffer; both at once (one iteration) stays generic
+        epi_axpy_body<TI, FIRST, LAST, false, IoRuntime>(x, acc, row0, col0, lane, stg);
+    } else if constexpr (FIRST) {
+        auto go = [&](auto dtc) __attribute__((always_inline)) {
+            constexpr int D = decltype(dtc)::value;
+            if (v.has_mom && !v.nest)
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, false, false, false>>(x, acc, row0, col0, lane, stg);
+            else if (v.has_mom)
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, true, false, false>>(x, acc, row0, col0, lane, stg);
+            else
+                epi_axpy_body<TI, true, false, false, IoFixed<D, false, false, false, false>>(x, acc, row0, col0, lane, stg);
+        };
+        if (v.dt == 0) go(std::integral_constant<int, 0>{});
+        else go(std::integral_constant<int, 1>{});
+    } else {
+        auto go = [&](auto dtc) __attribute__((always_inline)) {
+            constexpr int D = decltype(dtc)::value;
+            if (v.has_param && !v.upd)
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, false>>(x, acc, row0, col0, lane, stg);
+            else if (v.has_param)
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, true>>(x, acc, row0, col0, lane, stg);
+            else if (v.upd)
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, false, true>>(x, acc, row0, col0, lane, stg);
+            else
+                epi_axpy_body<TI, false, true, false, IoRuntime>(x, acc, row0, col0, lane, stg);
+        };
+        if (v.dt == 0) go(std::integral_constant<int, 0>{});
+        else go(std::integral_constant<int, 1>{});
+    }
 }
 
-// ---- GRAM (A = s^2 X X^T) and POLY (B / a = (b A + c A A) / a): upper triangle written
-// to (r, c) by the row-major pass and mirrored to (c, r) by the column-major
-// pass (diagonal tiles: r <= c, and r < c for the mirror).
+// ---- GRAM (A = s^2 X X^T) and POLY (B / a = (b A + c A A) / a): the upper
+// triangle is written by a row pass and mirrored by a second pass, so both the
+// stored matrix and its padding are exactly symmetric.
+//
+// Row pass: band by band (16 rows), the fp32 accumulators are staged in LDS
+// ([16][WT] floats, 16-float groups XOR-swizzled by row) and read back as runs
+// of 4 consecutive columns, combined (POLY: b A + c acc) and stored along rows.
+// Each rounded value is also written to the wave's transposed bf16 copy of its
+// tile in LDS, T[c][r] (8-element blocks of r XOR-swizzled by c).  Mirror pass:
+// rows of T are stored as 16-byte runs along the destination rows, so the
+// transposed block is written with the same coalescing as the row pass.
+// Padding rows and columns hold zeros on both sides (the operands' padding is
+// zero), so no access needs a bounds check; diagonal tiles write r <= c in the
+// row pass and r < c in the mirror pass.
 struct SymCtx {
     uint16_t* out;
     const uint16_t* ain;
     int64_t ldq;
-    int m;
     bool diag;
     float scl, b, c;
 };
 
-// A values a band needs (POLY): rows r, columns c..c+3 (row pass) and, by
-// symmetry, A[c][r..r+3] (mirror pass); padded, so always in bounds
 template <int TI>
-__device__ __forceinline__ void sym_load(const SymCtx& x, int row0, int col0, int lane, int band,
-                                         f32x4_t (&ar)[EpiGeom<TI>::NQ], f32x4_t (&am)[EpiGeom<TI>::NQ]) {
+struct SymGeom {
+    static constexpr int WT = TI * 16;
+    static constexpr int NQ = WT / 16;              // row-pass runs per lane per band
+    static constexpr int BPR = WT / 8;              // 8-element blocks per row of T
+    static constexpr int NM = WT * BPR / 64;        // mirror runs per lane
+    static constexpr int HM = BPR < 16 ? BPR - 1 : 15;
+    static constexpr int STG_BYTES = 16 * WT * 4;   // band staging per wave
+    static constexpr int T_BYTES = WT * WT * 2;     // transposed tile per wave
+};
+
+__device__ __forceinline__ int stg_swz(int r) { return 16 * ((r >> 2) & 3); }
+
+template <int TI>
+__device__ __forceinline__ void stage_band_sw(float* __restrict__ stg, const f32x4_t (&acc)[TI][TI], int i, int lane) {
+    constexpr int WT = SymGeom<TI>::WT;
+    const int g = lane >> 4, c16 = lane & 15;
 #pragma unroll
-    for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
-        int lr, lc, quad, lc2;
-        row_run<TI>(q, lane, lr, lc);
-        col_run<TI>(q, lane, quad, lc2);
-        ar[q] = ld4_bf16(x.ain + int64_t(row0 + 16 * band + lr) * x.ldq + col0 + lc);
-        am[q] = ld4_bf16(x.ain + int64_t(col0 + lc2) * x.ldq + row0 + 16 * band + 4 * quad);
+    for (int j = 0; j < TI; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            stg[r * WT + ((16 * j + c16) ^ stg_swz(r))] = acc[i][j][e];
+        }
+}
+
+// T[c][r]: block r / 8 of row c stored at block (r / 8) ^ h(c)
+template <int TI>
+__device__ __forceinline__ int t_index(int c, int r) {
+    const int h = (c >> 2) & SymGeom<TI>::HM;
+    return c * SymGeom<TI>::WT + ((((r >> 3) ^ h) << 3) | (r & 7));
+}
+
+template <int TI, bool POLY>
+__device__ __forceinline__ void sym_load(const SymCtx& x, int row0, int col0, int lane, int band,
+                                         f32x4_t (&ar)[SymGeom<TI>::NQ]) {
+    if constexpr (POLY) {
+#pragma unroll
+        for (int q = 0; q < SymGeom<TI>::NQ; ++q) {
+            int lr, lc;
+            row_run<TI>(q, lane, lr, lc);
+            ar[q] = ld4_bf16(x.ain + int64_t(row0 + 16 * band + lr) * x.ldq + col0 + lc);
+        }
     }
 }
 
 template <int TI, bool POLY>
-__device__ __forceinline__ void sym_store(const SymCtx& x, const float* __restrict__ stg, int row0, int col0, int lane,
-                                          int band, const f32x4_t (&ar)[EpiGeom<TI>::NQ],
-                                          const f32x4_t (&am)[EpiGeom<TI>::NQ]) {
-    using E = EpiGeom<TI>;
-    const int rb = row0 + 16 * band;
+__device__ __forceinline__ void sym_rows(const SymCtx& x, const float* __restrict__ stg, uint16_t* __restrict__ tt,
+                                         int row0, int col0, int lane, int band,
+                                         const f32x4_t (&ar)[SymGeom<TI>::NQ]) {
+    constexpr int WT = SymGeom<TI>::WT;
 #pragma unroll
-    for (int q = 0; q < E::NQ; ++q) {   // row-major pass: (r, c..c+3)
+    for (int q = 0; q < SymGeom<TI>::NQ; ++q) {
         int lr, lc;
         row_run<TI>(q, lane, lr, lc);
-        const int r = rb + lr, c = col0 + lc;
-        if (r >= x.m) continue;
-        int nv = x.m - c;
-        nv = nv > 4 ? 4 : nv;
-        const int first = (x.diag && r > c) ? r - c : 0;
-        if (nv <= first) continue;
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
-        const f32x4_t w = POLY ? x.b * ar[q] + x.c * v : v * x.scl;
-        const int64_t o = int64_t(r) * x.ldq + c;
-        if (nv == 4 && first == 0)
-            st4_bf16(x.out + o, w);
-        else
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * WT + (lc ^ stg_swz(lr)));
+        f32x4_t w;
+        if constexpr (POLY) w = x.b * ar[q] + x.c * v;
+        else w = v * x.scl;
+        uint16_t h[4];
 #pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                if (q2 >= first && q2 < nv) x.out[o + q2] = f32_to_bf16(w[q2]);
+        for (int k = 0; k < 4; ++k) h[k] = f32_to_bf16(w[k]);
+        const int rl = 16 * band + lr;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tt[t_index<TI>(lc + k, rl)] = h[k];
+        const int r = row0 + rl, c = col0 + lc;
+        GMEM uint16_t* o = gm(x.out + int64_t(r) * x.ldq + c);
+        if (!x.diag || r <= c) {
+            *reinterpret_cast<GMEM u32x2_t*>(o) = u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                                          uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+        } else {
+#pragma unroll
+            for (int k = 1; k < 4; ++k)
+                if (r <= c + k) o[k] = h[k];
+        }
     }
+}
+
+template <int TI>
+__device__ __forceinline__ void sym_mirror(const SymCtx& x, const uint16_t* __restrict__ tt, int row0, int col0,
+                                           int lane) {
+    using G = SymGeom<TI>;
 #pragma unroll
-    for (int q = 0; q < E::NQ; ++q) {   // mirror pass: (r..r+3, c) -> (c, r..r+3)
-        int quad, lc;
-        col_run<TI>(q, lane, quad, lc);
-        const int r = rb + 4 * quad, c = col0 + lc;
-        if (c >= x.m) continue;
-        int nv = x.m - r;
-        nv = nv > 4 ? 4 : nv;
-        if (x.diag) nv = nv < c - r ? nv : c - r;
-        if (nv <= 0) continue;
-        f32x4_t v;
+    for (int q = 0; q < G::NM; ++q) {
+        const int u = q * 64 + lane;
+        const int cl = u / G::BPR, blk = u % G::BPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tt + t_index<TI>(cl, 8 * blk));
+        const int r = row0 + 8 * blk, c = col0 + cl;   // destination (c, r..r+7)
+        GMEM uint16_t* o = gm(x.out + int64_t(c) * x.ldq + r);
+        if (!x.diag || r + 7 < c) {
+            *reinterpret_cast<GMEM u32x4_t*>(o) = v;
+        } else if (r < c) {
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) v[q2] = stg[(4 * quad + q2) * E::LDW + lc];
-        const f32x4_t w = POLY ? x.b * am[q] + x.c * v : v * x.scl;
-        const int64_t o = int64_t(c) * x.ldq + r;
-        if (nv == 4)
-            st4_bf16(x.out + o, w);
-        else
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2)
-                if (q2 < nv) x.out[o + q2] = f32_to_bf16(w[q2]);
+            for (int k = 0; k < 8; ++k)
+                if (r + k < c) o[k] = uint16_t(v[k >> 1] >> (16 * (k & 1)));
+        }
     }
 }
 
 template <int KIND, int TI>
 __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                        float* __restrict__ stg) {
-    constexpr int NQ = EpiGeom<TI>::NQ;
+                                        char* __restrict__ wlds) {
+    constexpr int NQ = SymGeom<TI>::NQ;
     constexpr bool POLY = KIND == PH_POLY;
+    float* stg = reinterpret_cast<float*>(wlds);
+    uint16_t* tt = reinterpret_cast<uint16_t*>(wlds + SymGeom<TI>::STG_BYTES);
     SymCtx x;
     x.out = reinterpret_cast<uint16_t*>(pa.ws + (KIND == PH_GRAM ? md.off_a : md.off_b));
     x.ain = reinterpret_cast<const uint16_t*>(pa.ws + md.off_a);
     x.ldq = md.mp;
-    x.m = md.m;
     x.diag = t.ti == t.tj;
     x.scl = 1.f;
     if (KIND == PH_GRAM && pa.iter == 1) {
@@ -1133,26 +1227,27 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     // stores B / a and AXPY scales the sum by a: X' = a (X + (B / a) X)
     x.b = pa.b / pa.a;
     x.c = pa.c / pa.a;
-    f32x4_t ar[2][NQ], am[2][NQ];
-    if (POLY) sym_load<TI>(x, row0, col0, lane, 0, ar[0], am[0]);
+    f32x4_t ar[2][NQ];
+    sym_load<TI, POLY>(x, row0, col0, lane, 0, ar[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (POLY && i + 1 < TI) sym_load<TI>(x, row0, col0, lane, i + 1, ar[(i + 1) & 1], am[(i + 1) & 1]);
-        stage_band<TI>(stg, acc, i, lane);
-        sym_store<TI, POLY>(x, stg, row0, col0, lane, i, ar[i & 1], am[i & 1]);
+        if constexpr (i + 1 < TI) sym_load<TI, POLY>(x, row0, col0, lane, i + 1, ar[(i + 1) & 1]);
+        stage_band_sw<TI>(stg, acc, i, lane);
+        sym_rows<TI, POLY>(x, stg, tt, row0, col0, lane, i, ar[i & 1]);
     });
+    sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
 template <int KIND, int TI, bool FIRST>
 __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                                 const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                                float* __restrict__ stg) {
+                                                char* __restrict__ wlds) {
     if constexpr (KIND == PH_AXPY)
-        epi_axpy<TI, FIRST, false>(md, t, pa, acc, row0, col0, lane, stg);
+        epi_axpy<TI, FIRST, false>(md, t, pa, acc, row0, col0, lane, reinterpret_cast<float*>(wlds));
     else if constexpr (KIND == PH_AXPY_LAST)
-        epi_axpy<TI, FIRST, true>(md, t, pa, acc, row0, col0, lane, stg);
+        epi_axpy<TI, FIRST, true>(md, t, pa, acc, row0, col0, lane, reinterpret_cast<float*>(wlds));
     else
-        epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, stg);
+        epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, wlds);
 }
 
 // ---- AXPY with a master-seeded accumulator (swapped MFMA layout: lane holds
@@ -1269,7 +1364,13 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
                                                             int n_tiles) {
     using C = BfCfg<BM, kBK>;
     constexpr int TI = C::TI, WT = C::WT;
-    __shared__ __attribute__((aligned(1024))) char smem[C::NST * C::STB];
+    // operand stages; afterwards the epilogue's per-wave regions
+    constexpr int EPI_AXPY_BYTES = 16 * (WT + 4) * 4;
+    constexpr int EPI_SYM_BYTES = SymGeom<TI>::STG_BYTES + SymGeom<TI>::T_BYTES;
+    constexpr int EPI_BYTES = 4 * (KIND == PH_AXPY || KIND == PH_AXPY_LAST ? EPI_AXPY_BYTES : EPI_SYM_BYTES);
+    constexpr int LDS_BYTES = C::NST * C::STB > EPI_BYTES ? C::NST * C::STB : EPI_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
     const MatDesc& md = mats[t.mat];
@@ -1305,8 +1406,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
         else
             mainloop<BM, kBK, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
-                                         reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
+        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_AXPY_BYTES);
     } else {
         // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
         if (KIND == PH_POLY || (op.a_kc && op.b_kc))
@@ -1314,8 +1414,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
         else
             mainloop<BM, kBK, false, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane,
-                                         reinterpret_cast<float*>(smem) + wave * 16 * (WT + 4));
+        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
     }
 }
 
