@@ -242,10 +242,13 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         geom[i] = d;
     }
 
-    // Newton-Schulz tile lists.  One tile edge per phase for the whole call:
-    // the large tile when it still yields a couple of workgroups per CU.
-    // GRAM/POLY: upper triangle of the m x m product; AXPY: the stored R x C
-    // shape (X is kept in the caller's orientation, transposed matrices as X^T)
+    // Newton-Schulz tile lists.  One tile edge per phase for the whole call.
+    // GRAM/POLY (upper triangle of the m x m product): 128-wide tiles, two
+    // workgroups per CU, so one tile's mirrored epilogue overlaps another's
+    // main loop (measured faster than 256-wide tiles at every workload size).
+    // AXPY (the stored R x C shape; X is kept in the caller's orientation,
+    // transposed matrices as X^T): the 256-wide tile once the phase still
+    // yields a couple of workgroups per CU.
     auto count_tiles = [&](int T, bool gram) {
         int64_t c = 0;
         for (const MatDesc& d : geom) {
@@ -256,7 +259,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     };
     int gram_tile = kTileF32, axpy_tile = kTileF32;
     if (!f32c) {
-        gram_tile = count_tiles(kTileLarge, true) >= MUON_LARGE_TILE_MIN_TILES ? kTileLarge : kTileSmall;
+        gram_tile = kTileSmall;
         axpy_tile = count_tiles(kTileLarge, false) >= MUON_LARGE_TILE_MIN_TILES ? kTileLarge : kTileSmall;
     }
     // Matrices with the longest k loops first (the hardware dispatches in

@@ -84,7 +84,8 @@ hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* m
                                 PhaseArgs a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 // Tile edges of the Newton-Schulz GEMMs: fp32 mode uses kTileF32; bf16 mode
-// picks kTileLarge or kTileSmall per phase from the tile count.
+// uses kTileSmall for GRAM/POLY and kTileLarge or kTileSmall for AXPY from
+// the tile count.
 constexpr int kTileF32 = 128;
 constexpr int kTileLarge = 256;
 constexpr int kTileSmall = 128;

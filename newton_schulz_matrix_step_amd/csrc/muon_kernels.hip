@@ -1494,19 +1494,25 @@ static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDes
 template <int KIND>
 static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
                         hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (f32c)
+    if (f32c) {
         hipExtLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0, tiles,
                               mats, a);
-    else if (tile == 256)
-        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
-    else
-        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
+        return;
+    }
+    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+        if (tile == 256) {
+            launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
+            return;
+        }
+    }
+    launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    if (f32c ? tile != 128 : (tile != 128 && tile != 256)) return hipErrorInvalidValue;
+    const bool axpy = kind == PH_AXPY || kind == PH_AXPY_LAST;
+    if (tile != 128 && !(tile == 256 && axpy && !f32c)) return hipErrorInvalidValue;
     switch (kind) {
         case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
