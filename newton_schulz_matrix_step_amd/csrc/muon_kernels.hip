@@ -590,19 +590,21 @@ __device__ __forceinline__ int kswz(int k) { return ((2 * k) & 6) | ((((k >> 3) 
 template <int CPK>
 __device__ __forceinline__ int kcswz(int r) { return CPK == 8 ? (r & 7) : ((r >> 1) & 3); }
 
-#ifndef MUON_LDS_DMA16
+#ifndef MUON_LDS_DMA16S
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
-// at lds + 16 L (lds must be wave-uniform).  Nothing is returned in registers;
-// completion is tracked by vmcnt and waited for with vm_wait().
-__device__ __forceinline__ void lds_dma16(const void* g, char* lds) {
+// 16 bytes per lane from global memory straight into LDS, from address
+// sbase + voff (sbase wave-uniform, in SGPRs; voff per lane): lane L's bytes
+// land at lds + 16 L (lds must be wave-uniform).  Nothing is returned in
+// registers; completion is tracked by vmcnt and waited for with vm_wait().
+__device__ __forceinline__ void lds_dma16s(const char* sbase, uint32_t voff, char* lds) {
     const uint32_t a = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)lds)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(a), "v"(g) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(a), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
 }
 #pragma clang diagnostic pop
 #else
-#define lds_dma16 MUON_LDS_DMA16
+#define lds_dma16s MUON_LDS_DMA16S
 #endif
 
 // s_waitcnt vmcnt(N), no wait on the other counters (gfx9 encoding).
@@ -612,26 +614,35 @@ __device__ __forceinline__ void vm_wait() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Issue the loads of one operand of one stage.
+// Issue the loads of one operand of one stage.  Row-contiguous (KC) operand:
+// 1 KB block blk holds rows blk * 64/CPK ..; a lane's row within the block and
+// its swizzled chunk do not depend on blk (the swizzle's period divides the
+// block), so one per-lane offset serves every block and only the SGPR base
+// moves.  k-strided operand: 1 KB block blk holds k rows blk * RPK ..; the
+// chunk swizzle depends on k, so the per-lane offset is recomputed per block.
 template <int BM, int BK, bool KC>
 __device__ __forceinline__ void issue_operand(char* __restrict__ lds, const char* __restrict__ g, int64_t ld, int row0,
                                               int k0, int wave, int lane) {
     using C = BfCfg<BM, BK>;
+    if (KC) {
+        constexpr int RB = 64 / C::CPK;
+        const int rl = lane / C::CPK;
+        const int c = (lane % C::CPK) ^ kcswz<C::CPK>(rl);
+        const uint32_t voff = uint32_t(rl * ld * 2 + c * 16);
 #pragma unroll
-    for (int q = 0; q < C::LPW; ++q) {
-        const int blk = wave * C::LPW + q;
-        const char* src;
-        if (KC) {
-            // [row][CPK chunks]: 64 / CPK rows per 1 KB
-            const int r = blk * (64 / C::CPK) + lane / C::CPK;
-            const int c = (lane % C::CPK) ^ kcswz<C::CPK>(r);
-            src = g + (int64_t(row0 + r) * ld + k0 + c * 8) * 2;
-        } else {
-            const int k = blk * C::RPK + lane / C::CPR;
-            const int c = (lane % C::CPR) ^ kswz(k);
-            src = g + (int64_t(k0 + k) * ld + row0 + c * 8) * 2;
+        for (int q = 0; q < C::LPW; ++q) {
+            const int blk = wave * C::LPW + q;
+            lds_dma16s(g + (int64_t(row0 + blk * RB) * ld + k0) * 2, voff, lds + blk * 1024);
         }
-        lds_dma16(src, lds + blk * 1024);
+    } else {
+        const int kl = lane / C::CPR;
+#pragma unroll
+        for (int q = 0; q < C::LPW; ++q) {
+            const int blk = wave * C::LPW + q;
+            const int c = (lane % C::CPR) ^ kswz(blk * C::RPK + kl);
+            const uint32_t voff = uint32_t(kl * ld * 2 + c * 16);
+            lds_dma16s(g + (int64_t(k0 + blk * C::RPK) * ld + row0) * 2, voff, lds + blk * 1024);
+        }
     }
 }
 
