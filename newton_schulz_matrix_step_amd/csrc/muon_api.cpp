@@ -42,8 +42,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
 #ifndef MUON_LARGE_TILE_MIN_TILES
-#define MUON_LARGE_TILE_MIN_TILES 512   // large tiles once a phase has this many of them
+#define MUON_LARGE_TILE_MIN_TILES 512   // large AXPY tiles only with at least this many of them
 #endif
+#ifndef MUON_LONG_K
+#define MUON_LONG_K 3072                // AXPY k (= m) from which 256-wide tiles pay off
+#endif
+constexpr int kLongK = MUON_LONG_K;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -247,20 +251,23 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     // workgroups per CU, so one tile's mirrored epilogue overlaps another's
     // main loop (measured faster than 256-wide tiles at every workload size).
     // AXPY (the stored R x C shape; X is kept in the caller's orientation,
-    // transposed matrices as X^T): the 256-wide tile once the phase still
-    // yields a couple of workgroups per CU.
-    auto count_tiles = [&](int T, bool gram) {
-        int64_t c = 0;
-        for (const MatDesc& d : geom) {
-            const int64_t tm = (d.m + T - 1) / T;
-            c += gram ? tm * (tm + 1) / 2 : int64_t((d.R + T - 1) / T) * ((d.C + T - 1) / T);
-        }
-        return c;
-    };
+    // transposed matrices as X^T; k = m): 256-wide tiles, which halve the
+    // operand traffic per flop, pay off once most of the flops sit in long-k
+    // matrices (m >= 3072 here) and the phase still has a couple of tiles per
+    // CU; with shorter k the 128-wide tiles win, their epilogues overlapping
+    // the other workgroup's main loop.
     int gram_tile = kTileF32, axpy_tile = kTileF32;
     if (!f32c) {
         gram_tile = kTileSmall;
-        axpy_tile = count_tiles(kTileLarge, false) >= MUON_LARGE_TILE_MIN_TILES ? kTileLarge : kTileSmall;
+        double flops = 0, long_k = 0;
+        int64_t large_tiles = 0;
+        for (const MatDesc& d : geom) {
+            const double f = double(d.m) * d.m * d.n;
+            flops += f;
+            if (d.m >= kLongK) long_k += f;
+            large_tiles += int64_t((d.R + kTileLarge - 1) / kTileLarge) * ((d.C + kTileLarge - 1) / kTileLarge);
+        }
+        axpy_tile = (2 * long_k > flops && large_tiles >= MUON_LARGE_TILE_MIN_TILES) ? kTileLarge : kTileSmall;
     }
     // Matrices with the longest k loops first (the hardware dispatches in
     // order, so the tail holds short tiles); within a matrix, groups of 4 tile

@@ -676,9 +676,6 @@ __device__ __forceinline__ void issue_stage(char* __restrict__ st, const Operand
     issue_operand<BM, BK, BKC>(st + BfCfg<BM, BK>::OPB, op.b, op.ldb, row_b0, k0, wave, lane);
 }
 
-// SWAP: feed the MFMA (B fragment, A fragment) so that each lane accumulates 4
-// consecutive output columns of one row (acc[i][j][e] = C[16 i + (lane & 15)]
-// [16 j + 4 (lane >> 4) + e]) instead of 4 consecutive rows of one column.
 // Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1, so
 // array indices derived from I stay constant whatever the unroller decides.
 template <int B, int E, class F>
@@ -689,7 +686,7 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int BM, int BK, bool AKC, bool BKC, bool SWAP>
+template <int BM, int BK, bool AKC, bool BKC>
 __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
                                          int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI]) {
     using C = BfCfg<BM, BK>;
@@ -725,8 +722,7 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TI; ++j)
-                    acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
-                                     : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             // issue every fragment read of the step before the MFMAs that consume them
             constexpr int kReads = TI * ((AKC ? 1 : 2) + (BKC ? 1 : 2));
             __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // LDS reads
@@ -1261,112 +1257,6 @@ __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t
         epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, wlds);
 }
 
-// ---- AXPY with a master-seeded accumulator (swapped MFMA layout: lane holds
-// C[r][c..c+3] with r = row0 + 16 i + (lane & 15), c = col0 + 16 j + 4 (lane >> 4)).
-template <int TI, bool FIRST>
-__device__ __forceinline__ void axpy_init(const MatDesc& md, int row0, int col0, int lane, const PhaseArgs& pa,
-                                          f32x4_t (&acc)[TI][TI]) {
-    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-    if (!FIRST) {
-        const float* xm = reinterpret_cast<const float*>(pa.ws + md.off_xm);
-        const int64_t ld = md.Cp;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TI; ++j)   // padded buffer: always in bounds, zero outside R x C
-                acc[i][j] = *reinterpret_cast<const f32x4_t*>(xm + int64_t(row0 + 16 * i + l16) * ld + col0 + 16 * j + g4);
-    } else {
-        const IoView io = io_view(md, pa.nesterov != 0);
-        const int R = md.R, C = md.C;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TI; ++j) {
-                const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
-                acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                if (r < R && c < C) {
-                    int nv = C - c;
-                    nv = nv > 4 ? 4 : nv;
-                    acc[i][j] = u4_at(io, r, c, pa.beta, io.vio && nv == 4, nv);
-                }
-            }
-    }
-}
-
-template <int TI, bool FIRST, bool LAST>
-__device__ __forceinline__ void axpy_direct(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                            const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane) {
-    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
-    const float scale = pa.a * (FIRST ? pa.inv_norm[t.mat] : 1.f);
-    const int R = md.R, C = md.C;
-    if (!LAST) {
-        const int it = pa.iter;
-        float* xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
-        uint16_t* xb = reinterpret_cast<uint16_t*>(pa.ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
-        const int64_t ld = md.Cp;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TI; ++j) {
-                const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
-                if (r >= R || c >= C) continue;
-                const f32x4_t x = scale * acc[i][j];
-                const int64_t o = int64_t(r) * ld + c;
-                if (c + 4 <= C) {
-                    *reinterpret_cast<f32x4_t*>(xm + o) = x;
-                    st4_bf16(xb + o, x);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (c + q < C) {
-                            xm[o + q] = x[q];
-                            xb[o + q] = f32_to_bf16(x[q]);
-                        }
-                }
-            }
-        return;
-    }
-    // last iteration: W = W (1 - lr wd) - lr s O, and the optional fp32 O
-    const IoView io = io_view(md, false);
-    const bool vio = io.vio;
-    const float wdec = 1.f - pa.lr * pa.wd;
-    const float step = pa.lr * md.shape_scale;
-    f32x4_t wv[2][TI];
-    auto load_w = [&](int i, f32x4_t (&w)[TI]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < TI; ++j) {
-            const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
-            w[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (io.has_param && r < R && c < C) {
-                int nv = C - c;
-                nv = nv > 4 ? 4 : nv;
-                w[j] = ld4_io(io.param, int64_t(r) * io.ld_param + c, io.dt, vio && nv == 4, nv);
-            }
-        }
-    };
-    load_w(0, wv[0]);
-    static_for<0, TI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + 1 < TI) load_w(i + 1, wv[(i + 1) & 1]);   // one row block ahead
-#pragma unroll
-        for (int j = 0; j < TI; ++j) {
-            const int r = row0 + 16 * i + l16, c = col0 + 16 * j + g4;
-            if (r >= R || c >= C) continue;
-            int nv = C - c;
-            nv = nv > 4 ? 4 : nv;
-            const bool vec = vio && nv == 4;
-            const f32x4_t o = scale * acc[i][j];
-            if (io.has_param) {
-                f32x4_t w;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) w[q] = fmaf(-step, o[q], wv[i & 1][j][q] * wdec);
-                st4_io(io.param, int64_t(r) * io.ld_param + c, io.dt, vec, nv, w);
-            }
-            if (io.upd) st4_io(io.upd, int64_t(r) * io.ld_upd + c, 1, vec, nv, o);
-        }
-    });
-}
-
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
@@ -1398,32 +1288,19 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 #pragma unroll
         for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if constexpr ((KIND == PH_AXPY || KIND == PH_AXPY_LAST) && BM == 128) {
-        // accumulators start at the master X (loads issued before the operand
-        // loads, so their latency hides behind the pipeline fill); the MFMAs add
-        // (B / a) X and the epilogue only scales and stores
-        axpy_init<TI, FIRST>(md, row_a0 + wr, row_b0 + wc, lane, pa, acc);
+    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
         if (op.a_kc && op.b_kc)
-            mainloop<BM, kBK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         else
-            mainloop<BM, kBK, true, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
-        axpy_direct<TI, FIRST, KIND == PH_AXPY_LAST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane);
-        return;
-    } else if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
-        // 256-wide tiles: the accumulators fill all 256 AGPRs, so the master
-        // term is added in the LDS-staged epilogue instead
-        if (op.a_kc && op.b_kc)
-            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
-        else
-            mainloop<BM, kBK, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
         epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_AXPY_BYTES);
     } else {
         // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
         if (KIND == PH_POLY || (op.a_kc && op.b_kc))
-            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         else
-            mainloop<BM, kBK, false, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
         epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
     }
