@@ -150,9 +150,13 @@ def cpu_baseline(wl, grads_host, budget_s: float):
         cores = os.cpu_count() or 1
     hp = oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
                       ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c)
-    done_elems, t_used, k = 0, 0.0, 0
+    # whole passes over the matrix list (step 1's inputs) while the budget
+    # lasts; a pass that alone exceeds it stops early and is extrapolated
+    done_elems, t_used, k, passes = 0, 0.0, 0, 0
     total = sum(s.rows * s.cols for s in wl.mats)
-    while k < len(wl.mats) and t_used < budget_s:
+    weights = [min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats]
+    done_flops = 0
+    while t_used < budget_s:
         w = oracle.decode(grads_host["param"][k])
         g = oracle.decode(grads_host["grad0"][k])
         m = np.asarray(make_momentum(wl, k), dtype=np.float64)
@@ -160,18 +164,26 @@ def cpu_baseline(wl, grads_host, budget_s: float):
         oracle.muon_step_matrix(w, g, m, hp)
         t_used += time.perf_counter() - t0
         done_elems += wl.mats[k].rows * wl.mats[k].cols
+        done_flops += weights[k]
         k += 1
+        if k == len(wl.mats):
+            k = 0
+            passes += 1
     # extrapolate by Newton-Schulz flops (the oracle's cost is its dgemms)
-    from_flops = sum(min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats)
-    done_flops = sum(min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats[:k])
-    est_step_s = t_used * from_flops / max(done_flops, 1)
+    est_step_s = t_used * sum(weights) / max(done_flops, 1)
+    if passes:
+        what = f"{passes} full step(s) over all {len(wl.mats)} matrices"
+        if k:
+            what += f" plus {k} matrices"
+    else:
+        what = f"{k} of {len(wl.mats)} matrices of one step ({done_elems}/{total} elements)"
     return {
         "value": 1.0 / est_step_s,
         "unit": "steps/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{k} of {len(wl.mats)} matrices of step 1 ({done_elems}/{total} elements), "
-                  f"{t_used:.1f} s of float64 NumPy/OpenBLAS, extrapolated to a full step by Newton-Schulz flops",
+        "sample": f"{what} with step 1's inputs, {t_used:.1f} s of float64 NumPy/OpenBLAS; "
+                  "steps/s = Newton-Schulz flops of one step / flops done per second",
     }
 
 
@@ -296,7 +308,7 @@ def main():
     dom_avg_s = stats[dom][1] * 1e-3 / stats[dom][0]
     achieved = work["flops"][dom] / dom_avg_s / 1e12
     roofline = {
-        "kernel": f"ns_gemm_kernel ({dom})",
+        "kernel": f"ns_gemm_bf16 ({dom})" if wl.compute == "bf16" else f"ns_gemm_kernel ({dom})",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
