@@ -111,7 +111,7 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
 
 /* One Muon step over `n_mats` matrices (all steps above), enqueued on `stream`.
  * The first call for a given list of shapes/dtypes/compute mode builds a plan and
- * allocates the workspace (about 10 bytes per weight element in bf16 mode, plus
+ * allocates the workspace (about 8 bytes per weight element in bf16 mode, plus
  * two min(rows,cols)^2 bf16 squares per matrix); later calls with the same
  * signature allocate nothing.
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with

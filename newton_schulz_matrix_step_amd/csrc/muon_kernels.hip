@@ -423,8 +423,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
         const int64_t ldx = md.Cp;
         const float alpha = (it == 1) ? pa.inv_norm[t.mat] : 1.f;
         const bool nest = pa.nesterov != 0;
-        const float* xm = reinterpret_cast<const float*>(ws + (F32 ? off_cur : md.off_xm));
-        float* xm_out = reinterpret_cast<float*>(ws + md.off_xm);
+        const float* xm = reinterpret_cast<const float*>(ws + off_cur);   // fp32 mode: X itself
         char* xb_next = ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0);
         const float wdec = 1.f - pa.lr * pa.wd;
         const float step = pa.lr * md.shape_scale;
@@ -439,7 +438,6 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
                         const float master = (it == 1) ? u_at(md, r, c, pa.beta, nest) : xm[int64_t(r) * ldx + c];
                         const float v = alpha * fmaf(pa.a, master, acc[i][j][e]);
                         if (KIND == PH_AXPY) {
-                            if (!F32) xm_out[int64_t(r) * ldx + c] = v;
                             store_elem(xb_next, int64_t(r) * ldx + c, ODT, v);
                         } else {
                             if (md.has_param) {
@@ -849,7 +847,8 @@ __device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
 // iteration O = X' applied to the weight: W = W (1 - lr wd) - lr s O and the
 // optional fp32 copy of O.  Runs are 4 consecutive stored columns of one row.
 struct AxpyCtx {
-    float* xm;
+    const uint16_t* xhi;       // current X, bf16 (the operand copy this GEMM reads)
+    uint16_t* xlo;             // X - hi, bf16: with hi, the master copy of X
     uint16_t* xb_next;
     int64_t ldq;
     int R, C;
@@ -923,9 +922,9 @@ template <class M>
 __device__ __forceinline__ bool io_upd(const IoView& v) { if constexpr (M::fixed) return M::upd; else return v.upd != nullptr; }
 
 // Raw operands of one band of the AXPY epilogue, per 4-element run:
-//   ra: the master (workspace fp32) or, on the first iteration, m' (g without
-//       a momentum buffer);  rb: g on the first iteration with Nesterov;
-//   rc: W on the last iteration.
+//   ra: the master, hi words in [0..1] and lo words in [2..3] or, on the first
+//       iteration, m' (g without a momentum buffer);  rb: g on the first
+//       iteration with Nesterov;  rc: W on the last iteration.
 template <int TI>
 struct AxpyRaw {
     u32x4_t ra[EpiGeom<TI>::NQ], rb[EpiGeom<TI>::NQ], rc[EpiGeom<TI>::NQ];
@@ -944,8 +943,11 @@ __device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, 
         nv = nv > 4 ? 4 : nv;
         const bool in = !EDGE || (r < x.R && c < x.C);
         const bool vec = !EDGE || (x.vio && nv == 4);
-        if (!FIRST) {
-            w.ra[q] = *gm(reinterpret_cast<const u32x4_t*>(x.xm + int64_t(r) * x.ldq + c));   // padded: in bounds
+        if (!FIRST) {   // padded buffers: in bounds
+            const int64_t off = int64_t(r) * x.ldq + c;
+            const u32x2_t hi = *gm(reinterpret_cast<const u32x2_t*>(x.xhi + off));
+            const u32x2_t lo = *gm(reinterpret_cast<const u32x2_t*>(x.xlo + off));
+            w.ra[q] = u32x4_t{hi[0], hi[1], lo[0], lo[1]};
         } else {
             w.ra[q] = u32x4_t{0u, 0u, 0u, 0u};
             w.rb[q] = u32x4_t{0u, 0u, 0u, 0u};
@@ -981,7 +983,7 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         nv = nv > 4 ? 4 : nv;
         f32x4_t mst;
         if (!FIRST) {
-            mst = dec4(w.ra[q], 1);
+            mst = dec4(w.ra[q], 0) + dec4(u32x4_t{w.ra[q][2], w.ra[q][3], 0u, 0u}, 0);
         } else if (io_mom<M>(x.io)) {
             mst = dec4(w.ra[q], 1);
             if (io_nest<M>(x.io)) {
@@ -995,16 +997,26 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
         const f32x4_t o = x.alpha * (x.a * (mst + v));   // acc holds (B / a) X
         if (!LAST) {
+            // X' = hi + lo: hi its bf16 rounding, lo the bf16 rounding of the
+            // (exact) remainder
             const int64_t off = int64_t(r) * x.ldq + c;
+            uint16_t h[4], l[4];
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+                h[q2] = f32_to_bf16(o[q2]);
+                l[q2] = f32_to_bf16(o[q2] - bf16_to_f32(h[q2]));
+            }
             if (!EDGE || nv == 4) {
-                *gm(reinterpret_cast<f32x4_t*>(x.xm + off)) = o;
-                st4_bf16(x.xb_next + off, o);
+                *gm(reinterpret_cast<u32x2_t*>(x.xb_next + off)) =
+                    u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+                *gm(reinterpret_cast<u32x2_t*>(x.xlo + off)) =
+                    u32x2_t{uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16)};
             } else {
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
                     if (q2 < nv) {
-                        gm(x.xm)[off + q2] = o[q2];
-                        gm(x.xb_next)[off + q2] = f32_to_bf16(o[q2]);
+                        gm(x.xb_next)[off + q2] = h[q2];
+                        gm(x.xlo)[off + q2] = l[q2];
                     }
             }
         } else {
@@ -1041,7 +1053,8 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
                                          float* __restrict__ stg) {
     AxpyCtx x;
     const int it = pa.iter;
-    x.xm = reinterpret_cast<float*>(pa.ws + md.off_xm);
+    x.xhi = reinterpret_cast<const uint16_t*>(pa.ws + (((it - 2) & 1) ? md.off_xb1 : md.off_xb0));   // it >= 2
+    x.xlo = reinterpret_cast<uint16_t*>(pa.ws + md.off_xlo);
     x.xb_next = reinterpret_cast<uint16_t*>(pa.ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
     x.ldq = md.Cp;
     x.R = md.R;
