@@ -684,7 +684,9 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-template <int BM, int BK, bool AKC, bool BKC>
+// SWAP: feed the MFMA (B fragment, A fragment), so each lane accumulates 4
+// consecutive output columns of one row instead of 4 rows of one column.
+template <int BM, int BK, bool AKC, bool BKC, bool SWAP>
 __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
                                          int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI]) {
     using C = BfCfg<BM, BK>;
@@ -720,7 +722,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                                     : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             // issue every fragment read of the step before the MFMAs that consume them
             constexpr int kReads = TI * ((AKC ? 1 : 2) + (BKC ? 1 : 2));
             __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // LDS reads
@@ -1108,13 +1111,13 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
 // triangle is written by a row pass and mirrored by a second pass, so both the
 // stored matrix and its padding are exactly symmetric.
 //
-// Row pass: band by band (16 rows), the fp32 accumulators are staged in LDS
-// ([16][WT] floats, 16-float groups XOR-swizzled by row) and read back as runs
-// of 4 consecutive columns, combined (POLY: b A + c acc) and stored along rows.
-// Each rounded value is also written to the wave's transposed bf16 copy of its
-// tile in LDS, T[c][r] (8-element blocks of r XOR-swizzled by c).  Mirror pass:
-// rows of T are stored as 16-byte runs along the destination rows, so the
-// transposed block is written with the same coalescing as the row pass.
+// The main loop runs with swapped MFMA operands, so each lane holds 4
+// consecutive columns of one row: acc[i][j][e] = C[16 i + (lane & 15)]
+// [16 j + 4 (lane >> 4) + e].  Row pass, straight from registers: combine
+// (POLY: b A + c acc, A read in the same layout), round once, store 8 bytes
+// along the row, and write the 4 values into the wave's transposed bf16 copy of
+// its tile in LDS, T[c][r] (8-element blocks of r XOR-swizzled by c).  Mirror
+// pass: rows of T are stored as 16-byte runs along the destination rows.
 // Padding rows and columns hold zeros on both sides (the operands' padding is
 // zero), so no access needs a bounds check; diagonal tiles write r <= c in the
 // row pass and r < c in the mirror pass.
@@ -1129,79 +1132,17 @@ struct SymCtx {
 template <int TI>
 struct SymGeom {
     static constexpr int WT = TI * 16;
-    static constexpr int NQ = WT / 16;              // row-pass runs per lane per band
     static constexpr int BPR = WT / 8;              // 8-element blocks per row of T
     static constexpr int NM = WT * BPR / 64;        // mirror runs per lane
     static constexpr int HM = BPR < 16 ? BPR - 1 : 15;
-    static constexpr int STG_BYTES = 16 * WT * 4;   // band staging per wave
     static constexpr int T_BYTES = WT * WT * 2;     // transposed tile per wave
 };
-
-__device__ __forceinline__ int stg_swz(int r) { return 16 * ((r >> 2) & 3); }
-
-template <int TI>
-__device__ __forceinline__ void stage_band_sw(float* __restrict__ stg, const f32x4_t (&acc)[TI][TI], int i, int lane) {
-    constexpr int WT = SymGeom<TI>::WT;
-    const int g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int j = 0; j < TI; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            stg[r * WT + ((16 * j + c16) ^ stg_swz(r))] = acc[i][j][e];
-        }
-}
 
 // T[c][r]: block r / 8 of row c stored at block (r / 8) ^ h(c)
 template <int TI>
 __device__ __forceinline__ int t_index(int c, int r) {
     const int h = (c >> 2) & SymGeom<TI>::HM;
     return c * SymGeom<TI>::WT + ((((r >> 3) ^ h) << 3) | (r & 7));
-}
-
-template <int TI, bool POLY>
-__device__ __forceinline__ void sym_load(const SymCtx& x, int row0, int col0, int lane, int band,
-                                         f32x4_t (&ar)[SymGeom<TI>::NQ]) {
-    if constexpr (POLY) {
-#pragma unroll
-        for (int q = 0; q < SymGeom<TI>::NQ; ++q) {
-            int lr, lc;
-            row_run<TI>(q, lane, lr, lc);
-            ar[q] = ld4_bf16(x.ain + int64_t(row0 + 16 * band + lr) * x.ldq + col0 + lc);
-        }
-    }
-}
-
-template <int TI, bool POLY>
-__device__ __forceinline__ void sym_rows(const SymCtx& x, const float* __restrict__ stg, uint16_t* __restrict__ tt,
-                                         int row0, int col0, int lane, int band,
-                                         const f32x4_t (&ar)[SymGeom<TI>::NQ]) {
-    constexpr int WT = SymGeom<TI>::WT;
-#pragma unroll
-    for (int q = 0; q < SymGeom<TI>::NQ; ++q) {
-        int lr, lc;
-        row_run<TI>(q, lane, lr, lc);
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * WT + (lc ^ stg_swz(lr)));
-        f32x4_t w;
-        if constexpr (POLY) w = x.b * ar[q] + x.c * v;
-        else w = v * x.scl;
-        uint16_t h[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) h[k] = f32_to_bf16(w[k]);
-        const int rl = 16 * band + lr;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) tt[t_index<TI>(lc + k, rl)] = h[k];
-        const int r = row0 + rl, c = col0 + lc;
-        GMEM uint16_t* o = gm(x.out + int64_t(r) * x.ldq + c);
-        if (!x.diag || r <= c) {
-            *reinterpret_cast<GMEM u32x2_t*>(o) = u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
-                                                          uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-        } else {
-#pragma unroll
-            for (int k = 1; k < 4; ++k)
-                if (r <= c + k) o[k] = h[k];
-        }
-    }
 }
 
 template <int TI>
@@ -1229,10 +1170,8 @@ template <int KIND, int TI>
 __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                         char* __restrict__ wlds) {
-    constexpr int NQ = SymGeom<TI>::NQ;
     constexpr bool POLY = KIND == PH_POLY;
-    float* stg = reinterpret_cast<float*>(wlds);
-    uint16_t* tt = reinterpret_cast<uint16_t*>(wlds + SymGeom<TI>::STG_BYTES);
+    uint16_t* tt = reinterpret_cast<uint16_t*>(wlds);
     SymCtx x;
     x.out = reinterpret_cast<uint16_t*>(pa.ws + (KIND == PH_GRAM ? md.off_a : md.off_b));
     x.ain = reinterpret_cast<const uint16_t*>(pa.ws + md.off_a);
@@ -1247,14 +1186,45 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     // stores B / a and AXPY scales the sum by a: X' = a (X + (B / a) X)
     x.b = pa.b / pa.a;
     x.c = pa.c / pa.a;
-    f32x4_t ar[2][NQ];
-    sym_load<TI, POLY>(x, row0, col0, lane, 0, ar[0]);
-    static_for<0, TI>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + 1 < TI) sym_load<TI, POLY>(x, row0, col0, lane, i + 1, ar[(i + 1) & 1]);
-        stage_band_sw<TI>(stg, acc, i, lane);
-        sym_rows<TI, POLY>(x, stg, tt, row0, col0, lane, i, ar[i & 1]);
-    });
+    const int l16 = lane & 15, g4 = 4 * (lane >> 4);
+    u32x2_t av[TI][TI];
+    if constexpr (POLY) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TI; ++j)
+                av[i][j] = *gm(reinterpret_cast<const u32x2_t*>(x.ain + int64_t(row0 + 16 * i + l16) * x.ldq + col0 +
+                                                                16 * j + g4));
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TI; ++j) {
+            const int rl = 16 * i + l16, cl = 16 * j + g4;
+            f32x4_t w;
+            if constexpr (POLY) {
+                const f32x4_t a = dec4(u32x4_t{av[i][j][0], av[i][j][1], 0u, 0u}, 0);
+                w = x.b * a + x.c * acc[i][j];
+            } else {
+                w = acc[i][j] * x.scl;
+            }
+            uint16_t h[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                h[k] = f32_to_bf16(w[k]);
+                tt[t_index<TI>(cl + k, rl)] = h[k];
+            }
+            const int r = row0 + rl, c = col0 + cl;
+            GMEM uint16_t* o = gm(x.out + int64_t(r) * x.ldq + c);
+            if (!x.diag || r <= c) {
+                *reinterpret_cast<GMEM u32x2_t*>(o) = u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                                              uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+            } else {
+#pragma unroll
+                for (int k = 1; k < 4; ++k)
+                    if (r <= c + k) o[k] = h[k];
+            }
+        }
     sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
@@ -1280,7 +1250,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
     constexpr int TI = C::TI, WT = C::WT;
     // operand stages; afterwards the epilogue's per-wave regions
     constexpr int EPI_AXPY_BYTES = 16 * (WT + 4) * 4;
-    constexpr int EPI_SYM_BYTES = SymGeom<TI>::STG_BYTES + SymGeom<TI>::T_BYTES;
+    constexpr int EPI_SYM_BYTES = SymGeom<TI>::T_BYTES;
     constexpr int EPI_BYTES = 4 * (KIND == PH_AXPY || KIND == PH_AXPY_LAST ? EPI_AXPY_BYTES : EPI_SYM_BYTES);
     constexpr int LDS_BYTES = C::NST * C::STB > EPI_BYTES ? C::NST * C::STB : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -1303,17 +1273,17 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 
     if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
         if (op.a_kc && op.b_kc)
-            mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         else
-            mainloop<BM, kBK, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
         epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_AXPY_BYTES);
     } else {
         // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
         if (KIND == PH_POLY || (op.a_kc && op.b_kc))
-            mainloop<BM, kBK, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         else
-            mainloop<BM, kBK, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, kBK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
         epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
     }
