@@ -49,6 +49,7 @@ constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (targ
 #endif
 constexpr int kLongK = MUON_LONG_K;
 
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct Plan {
@@ -60,9 +61,13 @@ struct Plan {
     std::vector<MatDesc> uploaded; // last descriptor table sent to the device
     bool have_uploaded = false;
     MatDesc* d_desc = nullptr;
+    // tile lists: 8 per-XCD chunks of equal length (n_* = 8 x chunk), padded
+    // with skip entries (mat = -1)
     Tile* d_gram = nullptr;
     int n_gram = 0;
     int gram_tile = 0;
+    Tile* d_poly = nullptr;
+    int n_poly = 0;
     Tile* d_axpy = nullptr;
     int n_axpy = 0;
     int axpy_tile = 0;
@@ -132,6 +137,7 @@ struct DeviceGuard {
 void free_plan(Plan& p) {
     (void)hipFree(p.d_desc);
     (void)hipFree(p.d_gram);
+    (void)hipFree(p.d_poly);
     (void)hipFree(p.d_axpy);
     (void)hipFree(p.d_units);
     (void)hipFree(p.d_partials);
@@ -269,37 +275,80 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         }
         axpy_tile = (2 * long_k > flops && large_tiles >= MUON_LARGE_TILE_MIN_TILES) ? kTileLarge : kTileSmall;
     }
-    // Matrices with the longest k loops first (the hardware dispatches in
-    // order, so the tail holds short tiles); within a matrix, groups of 4 tile
-    // rows sweep the tile columns so concurrent tiles share operand panels.
-    std::vector<int> order(n);
-    for (int i = 0; i < n; ++i) order[i] = i;
-    auto build_list = [&](int T, bool gram, std::vector<Tile>& out) {
-        std::vector<int> ord = order;
-        std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) {
-            const int64_t kx = gram ? geom[x].n : geom[x].m, ky = gram ? geom[y].n : geom[y].m;
-            return kx > ky;
-        });
-        for (int i : ord) {
-            const MatDesc& d = geom[i];
+    // Tile lists.  Workgroup b runs on XCD b % 8, and each XCD has its own L2,
+    // so every list is 8 chunks, one per XCD: chunk x holds the tiles XCD x
+    // runs, in dispatch order.  Tiles come in items (one matrix's group of up
+    // to 4 tile rows across all tile columns, which share operand panels);
+    // items are dealt to the XCDs largest first, each to the least-loaded one
+    // (load = tiles x k blocks), so every XCD gets about the same work however
+    // mixed the matrix shapes (keeping a matrix on one XCD for L2 reuse
+    // measured slower: it costs balance); within a chunk, the longest-k tiles
+    // go first.
+    // GRAM (k = n) and POLY (k = m) weigh the same tiles differently, so each
+    // gets its own list.
+    auto build_list = [&](int T, int kind, std::vector<Tile>& out) {
+        const bool sym = kind != PH_AXPY;
+        struct Item {
+            int mat, a0;
+            int64_t w;
+        };
+        std::vector<Item> items;
+        auto ksteps = [&](const MatDesc& d) -> int64_t {
+            const int64_t K = kind == PH_GRAM ? d.n : d.m;
+            return (K + 63) / 64;
+        };
+        auto dims = [&](const MatDesc& d, int& tm, int& tn) {
             // GRAM/POLY outputs are m x m (upper triangle); AXPY outputs are R x C
-            const int tm = gram ? (d.m + T - 1) / T : (d.R + T - 1) / T;
-            const int tn = gram ? tm : (d.C + T - 1) / T;
-            for (int a0 = 0; a0 < tm; a0 += 4)
-                for (int b = 0; b < tn; ++b)
-                    for (int a = a0; a < std::min(tm, a0 + 4); ++a)
-                        if (!gram || b >= a) out.push_back(Tile{i, a, b, 0});
+            tm = sym ? (d.m + T - 1) / T : (d.R + T - 1) / T;
+            tn = sym ? tm : (d.C + T - 1) / T;
+        };
+        for (int i = 0; i < n; ++i) {
+            int tm, tn;
+            dims(geom[i], tm, tn);
+            for (int a0 = 0; a0 < tm; a0 += 4) {
+                int64_t cnt = 0;
+                for (int a = a0; a < std::min(tm, a0 + 4); ++a) cnt += sym ? tn - a : tn;
+                items.push_back(Item{i, a0, cnt * ksteps(geom[i])});
+            }
         }
+        std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.w > y.w; });
+        std::vector<Tile> bins[8];
+        int64_t load[8] = {};
+        for (const Item& it : items) {
+            int x = 0;
+            for (int c = 1; c < 8; ++c)
+                if (load[c] < load[x]) x = c;
+            load[x] += it.w;
+            int tm, tn;
+            dims(geom[it.mat], tm, tn);
+            for (int b = 0; b < tn; ++b)
+                for (int a = it.a0; a < std::min(tm, it.a0 + 4); ++a)
+                    if (!sym || b >= a) bins[x].push_back(Tile{it.mat, a, b, 0});
+        }
+        size_t chunk = 0;
+        for (auto& bin : bins) {
+            std::stable_sort(bin.begin(), bin.end(), [&](const Tile& x, const Tile& y) {
+                return ksteps(geom[x.mat]) > ksteps(geom[y.mat]);
+            });
+            chunk = std::max(chunk, bin.size());
+        }
+        out.assign(8 * chunk, Tile{-1, 0, 0, 0});
+        for (int x = 0; x < 8; ++x) std::copy(bins[x].begin(), bins[x].end(), out.begin() + x * chunk);
     };
-    build_list(gram_tile, true, gram);
-    build_list(axpy_tile, false, axpy);
+    std::vector<Tile> poly;
+    build_list(gram_tile, PH_GRAM, gram);
+    build_list(gram_tile, PH_POLY, poly);
+    build_list(axpy_tile, PH_AXPY, axpy);
     // every tile's operand panels must lie inside the padded workspace buffers
-    for (const Tile& t : gram) {
-        const MatDesc& d = geom[t.mat];
-        if ((t.ti + 1) * gram_tile > d.mp || (t.tj + 1) * gram_tile > d.mp || t.tj < t.ti)
-            return fail(h, MUON_ERR_HIP, "internal: gram tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
-    }
+    for (const std::vector<Tile>* lst : {&gram, &poly})
+        for (const Tile& t : *lst) {
+            if (t.mat < 0) continue;
+            const MatDesc& d = geom[t.mat];
+            if ((t.ti + 1) * gram_tile > d.mp || (t.tj + 1) * gram_tile > d.mp || t.tj < t.ti)
+                return fail(h, MUON_ERR_HIP, "internal: gram tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
+        }
     for (const Tile& t : axpy) {
+        if (t.mat < 0) continue;
         const MatDesc& d = geom[t.mat];
         if ((t.ti + 1) * axpy_tile > d.Rp || (t.tj + 1) * axpy_tile > d.Cp)
             return fail(h, MUON_ERR_HIP, "internal: axpy tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
@@ -313,6 +362,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     };
     bool ok = dmalloc(reinterpret_cast<void**>(&q.d_desc), sizeof(MatDesc) * n) &&
               dmalloc(reinterpret_cast<void**>(&q.d_gram), sizeof(Tile) * gram.size()) &&
+              dmalloc(reinterpret_cast<void**>(&q.d_poly), sizeof(Tile) * poly.size()) &&
               dmalloc(reinterpret_cast<void**>(&q.d_axpy), sizeof(Tile) * axpy.size()) &&
               dmalloc(reinterpret_cast<void**>(&q.d_units), sizeof(Unit) * units.size()) &&
               dmalloc(reinterpret_cast<void**>(&q.d_partials), sizeof(float) * units.size()) &&
@@ -331,6 +381,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     q.ws_bytes = off;
     hipError_t e = launch_fill_zero(q.ws, off, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(q.d_gram, gram.data(), sizeof(Tile) * gram.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(q.d_poly, poly.data(), sizeof(Tile) * poly.size(), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(q.d_axpy, axpy.data(), sizeof(Tile) * axpy.size(), hipMemcpyHostToDevice, stream);
     if (e == hipSuccess) e = hipMemcpyAsync(q.d_units, units.data(), sizeof(Unit) * units.size(), hipMemcpyHostToDevice, stream);
     // the host vectors die with this call: wait for the copies
@@ -343,6 +394,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     q.f32c = f32c;
     q.geom = std::move(geom);
     q.n_gram = int(gram.size());
+    q.n_poly = int(poly.size());
     q.n_axpy = int(axpy.size());
     q.gram_tile = gram_tile;
     q.axpy_tile = axpy_tile;
@@ -475,7 +527,7 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
         });
         if (e != hipSuccess) return hip_fail(h, e, "gram launch");
         e = timed(h, K_POLY, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream, e0, e1);
+            return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_poly, plan.n_poly, plan.d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "poly launch");
         const bool last = it == hp->ns_steps;

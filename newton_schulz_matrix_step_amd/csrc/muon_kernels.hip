@@ -452,13 +452,9 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
     }
 }
 
-// Workgroups are handed to the 8 XCDs round-robin; give each XCD a contiguous
-// range of the tile list so neighbouring tiles share that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int bid, int n) {
-    const int q = n >> 3, r = n & 7;
-    const int x = bid & 7, idx = bid >> 3;
-    return (x < r) ? x * (q + 1) + idx : r * (q + 1) + (x - r) * q + idx;
-}
+// Workgroup b runs on XCD b % 8.  Tile lists hold 8 equal chunks, chunk x
+// being the tiles XCD x runs in dispatch order; padding entries have mat < 0.
+__device__ __forceinline__ int xcd_tile(int bid, int n_tiles) { return (bid & 7) * (n_tiles >> 3) + (bid >> 3); }
 
 // ---------------------------------------------------------------------------
 // fp32 validation-mode GEMM: 128 x 128 tiles, register-staged loads
@@ -471,7 +467,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
     __shared__ u32x4_t sA[2][BM * 8];
     __shared__ u32x4_t sB[2][BM * 8];
 
-    const Tile t = tiles[blockIdx.x];
+    const Tile t = tiles[xcd_tile(blockIdx.x, gridDim.x)];
+    if (t.mat < 0) return;
     const MatDesc& md = mats[t.mat];
     const Operands op = resolve_operands<KIND>(md, pa);
 
@@ -1257,6 +1254,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
+    if (t.mat < 0) return;
     const MatDesc& md = mats[t.mat];
     const Operands op = resolve_operands<KIND>(md, pa);
 
