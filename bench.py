@@ -131,10 +131,15 @@ def copy_calibration(mib: int, reps: int = 5):
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
     for _ in range(reps):
         dst.copy_(src)
+    e1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes": n * 4, "reps": reps}), flush=True)
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps, "ms_per_copy": round(ms, 4),
+                      "read_plus_write_gbs": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(wl, grads_host, budget_s: float):

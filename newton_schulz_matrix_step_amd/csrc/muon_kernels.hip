@@ -121,57 +121,93 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
     float ss = 0.f;
 
     if (md.vec_ok) {
+        // kU groups of 8 columns per thread per pass: every load of the pass is
+        // issued before the first use, so each thread keeps kU x 48 bytes in flight
+#ifndef MUON_MOM_UNROLL
+#define MUON_MOM_UNROLL 4
+#endif
+        constexpr int kU = MUON_MOM_UNROLL;
         const int gpr = C >> 3;  // groups of 8 columns per row
         const int total = rows * gpr;
-        for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-            const int rr = idx / gpr;
-            const int c = (idx - rr * gpr) << 3;
-            const int64_t r = un.r0 + rr;
-            float g[8];
-            if (md.io_dtype == 0) {
-                const u32x4_t v = *gm(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(md.grad) + r * md.ld_grad + c));
+        const bool bf = md.io_dtype == 0;
+        const GMEM char* gbase = gm(static_cast<const char*>(md.grad));
+        GMEM float* mbase = gm(md.mom);
+        for (int base = threadIdx.x; base < total; base += kThreads * kU) {
+            u32x4_t graw[kU][2];
+            f32x4_t mv[kU][2];
+            int64_t row[kU];
+            int col[kU];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    g[2 * q] = __uint_as_float(v[q] << 16);
-                    g[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+            for (int u = 0; u < kU; ++u) {
+                const int idx = base + u * kThreads;
+                const int rr = idx < total ? idx / gpr : 0;
+                row[u] = un.r0 + rr;
+                col[u] = (idx - rr * gpr) << 3;
+                if (idx < total) {
+                    if (bf) {
+                        graw[u][0] = *reinterpret_cast<const GMEM u32x4_t*>(gbase + (row[u] * md.ld_grad + col[u]) * 2);
+                    } else {
+                        const GMEM u32x4_t* gp = reinterpret_cast<const GMEM u32x4_t*>(gbase + (row[u] * md.ld_grad + col[u]) * 4);
+                        graw[u][0] = gp[0];
+                        graw[u][1] = gp[1];
+                    }
+                    if (has_mom) {
+                        const GMEM f32x4_t* mp = reinterpret_cast<const GMEM f32x4_t*>(mbase + row[u] * md.ld_mom + col[u]);
+                        mv[u][0] = mp[0];
+                        mv[u][1] = mp[1];
+                    }
                 }
-            } else {
-                const GMEM f32x4_t* gp = gm(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(md.grad) + r * md.ld_grad + c));
-                const f32x4_t v0 = gp[0], v1 = gp[1];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) { g[q] = v0[q]; g[4 + q] = v1[q]; }
-            }
-            float u[8];
-            if (has_mom) {
-                GMEM f32x4_t* mp = gm(reinterpret_cast<f32x4_t*>(md.mom + r * md.ld_mom + c));
-                f32x4_t m0 = mp[0], m1 = mp[1];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    m0[q] = fmaf(beta, m0[q], g[q]);
-                    m1[q] = fmaf(beta, m1[q], g[4 + q]);
-                }
-                mp[0] = m0;
-                mp[1] = m1;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    u[q] = nest ? fmaf(beta, m0[q], g[q]) : m0[q];
-                    u[4 + q] = nest ? fmaf(beta, m1[q], g[4 + q]) : m1[q];
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) u[q] = g[q];
             }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) ss = fmaf(u[q], u[q], ss);
-            if (F32C) {
-                GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + r * ldu + c));
-                up[0] = f32x4_t{u[0], u[1], u[2], u[3]};
-                up[1] = f32x4_t{u[4], u[5], u[6], u[7]};
-            } else {
-                u32x4_t w;
+            for (int u = 0; u < kU; ++u) {
+                const int idx = base + u * kThreads;
+                if (idx >= total) continue;
+                float g[8];
+                if (bf) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(u[2 * q], u[2 * q + 1]);
-                *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + r * ldu + c)) = w;
+                    for (int q = 0; q < 4; ++q) {
+                        g[2 * q] = __uint_as_float(graw[u][0][q] << 16);
+                        g[2 * q + 1] = __uint_as_float(graw[u][0][q] & 0xFFFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        g[q] = __uint_as_float(graw[u][0][q]);
+                        g[4 + q] = __uint_as_float(graw[u][1][q]);
+                    }
+                }
+                float uu[8];
+                if (has_mom) {
+                    f32x4_t m0 = mv[u][0], m1 = mv[u][1];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        m0[q] = fmaf(beta, m0[q], g[q]);
+                        m1[q] = fmaf(beta, m1[q], g[4 + q]);
+                    }
+                    GMEM f32x4_t* mp = reinterpret_cast<GMEM f32x4_t*>(mbase + row[u] * md.ld_mom + col[u]);
+                    mp[0] = m0;
+                    mp[1] = m1;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uu[q] = nest ? fmaf(beta, m0[q], g[q]) : m0[q];
+                        uu[4 + q] = nest ? fmaf(beta, m1[q], g[4 + q]) : m1[q];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) uu[q] = g[q];
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) ss = fmaf(uu[q], uu[q], ss);
+                if (F32C) {
+                    GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + row[u] * ldu + col[u]));
+                    up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
+                    up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
+                } else {
+                    u32x4_t w;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(uu[2 * q], uu[2 * q + 1]);
+                    *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + row[u] * ldu + col[u])) = w;
+                }
             }
         }
     } else {
