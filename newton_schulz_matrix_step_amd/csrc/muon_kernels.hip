@@ -32,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -717,11 +718,74 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+template <int TI>
+struct EpiGeom {
+    static constexpr int WT = TI * 16;    // wave tile edge
+    static constexpr int LDW = WT + 4;    // padded LDS row (floats)
+    static constexpr int NQ = WT / 16;    // 4-element runs per lane per band
+};
+
+template <int TI>
+__device__ __forceinline__ void stage_band(float* __restrict__ stg, const f32x4_t (&acc)[TI][TI], int i, int lane) {
+    constexpr int LDW = EpiGeom<TI>::LDW;
+    const int g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < TI; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stg[(4 * g + e) * LDW + 16 * j + c16] = acc[i][j][e];
+}
+
+// Row-major pass geometry: run q of a lane covers band row lr, columns lc..lc+3.
+template <int TI>
+__device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
+    constexpr int WT = EpiGeom<TI>::WT;
+    const int idx = q * 256 + lane * 4;
+    lr = idx / WT;
+    lc = idx % WT;
+}
+
+// The bf16 copy of the master X that an AXPY output tile needs passes through
+// LDS as operand data during one k block (128-wide tiles: a wave's 64 x 64
+// quadrant is exactly one 64-deep block).  HiCap keeps it, in the epilogue's
+// run order (band i, run q: row 16 i + lr, columns lc..lc+3), so the epilogue
+// does not read it again from HBM.  CAP 1: X is the k-strided B operand
+// ([k][BM], quadrant rows = k); CAP 2: X is the row-contiguous A operand
+// ([row][k], quadrant columns = k).
+template <int TI>
+struct HiCap {
+    static constexpr int N = TI * 16 == 64 ? TI : 1;   // only quadrants of one 64-deep k block capture
+    u32x2_t v[N][N];
+    int kb;   // k block holding the quadrant
+};
+
+template <int BM, int BK, int CAP, int TI>
+__device__ __forceinline__ void capture_hi(const char* __restrict__ st, HiCap<TI>& cap, int wr, int wc, int lane) {
+    using C = BfCfg<BM, BK>;
+    static_for<0, TI>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+#pragma unroll
+        for (int q = 0; q < TI; ++q) {
+            int lr, lc;
+            row_run<TI>(q, lane, lr, lc);
+            int off;
+            if constexpr (CAP == 1) {
+                const int k = 16 * i + lr, n = wc + lc;
+                off = C::OPB + k * (BM * 2) + (((n >> 3) ^ kswz(k)) << 4) + (n & 7) * 2;
+            } else {
+                const int r = wr + 16 * i + lr, k = lc;
+                off = r * (C::CPK * 16) + (((k >> 3) ^ kcswz<C::CPK>(r)) << 4) + (k & 7) * 2;
+            }
+            cap.v[i][q] = *reinterpret_cast<const u32x2_t*>(st + off);
+        }
+    });
+}
+
 // SWAP: feed the MFMA (B fragment, A fragment), so each lane accumulates 4
 // consecutive output columns of one row instead of 4 rows of one column.
-template <int BM, int BK, bool AKC, bool BKC, bool SWAP>
+template <int BM, int BK, bool AKC, bool BKC, bool SWAP, int CAP = 0>
 __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
-                                         int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI]) {
+                                         int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI],
+                                         HiCap<BfCfg<BM, BK>::TI>* cap = nullptr) {
     using C = BfCfg<BM, BK>;
     constexpr int TI = C::TI;
     const int wr = (wave >> 1) * C::WT, wc = (wave & 1) * C::WT;
@@ -744,6 +808,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
                                           (kb + C::NST - 1) * C::BK, wave, lane);
         const char* sa = smem + (kb % C::NST) * C::STB;
         const char* sb = sa + C::OPB;
+        if constexpr (CAP != 0)
+            if (kb == cap->kb) capture_hi<BM, BK, CAP, TI>(sa, *cap, wr, wc, lane);
 #pragma unroll
         for (int s = 0; s < BK / 32; ++s) {
             bf16x8_t fa[TI], fb[TI];
@@ -765,7 +831,6 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
     }
 }
 
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t ld4_bf16(const void* p) {
     const u32x2_t w = *gm(reinterpret_cast<const u32x2_t*>(p));
@@ -853,31 +918,6 @@ __device__ __forceinline__ f32x4_t u4_at(const IoView& v, int64_t r, int64_t c, 
 // are issued before the current band is stored, so each lane keeps a band's
 // worth of loads in flight.
 
-template <int TI>
-struct EpiGeom {
-    static constexpr int WT = TI * 16;    // wave tile edge
-    static constexpr int LDW = WT + 4;    // padded LDS row (floats)
-    static constexpr int NQ = WT / 16;    // 4-element runs per lane per band
-};
-
-template <int TI>
-__device__ __forceinline__ void stage_band(float* __restrict__ stg, const f32x4_t (&acc)[TI][TI], int i, int lane) {
-    constexpr int LDW = EpiGeom<TI>::LDW;
-    const int g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int j = 0; j < TI; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) stg[(4 * g + e) * LDW + 16 * j + c16] = acc[i][j][e];
-}
-
-// Row-major pass geometry: run q of a lane covers band row lr, columns lc..lc+3.
-template <int TI>
-__device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
-    constexpr int WT = EpiGeom<TI>::WT;
-    const int idx = q * 256 + lane * 4;
-    lr = idx / WT;
-    lc = idx % WT;
-}
 // ---- AXPY: X' = alpha (a X + B X) on the stored R x C tile grid (see
 // resolve_operands): fp32 master and bf16 operand copy, or on the last
 // iteration O = X' applied to the weight: W = W (1 - lr wd) - lr s O and the
@@ -968,8 +1008,9 @@ struct AxpyRaw {
 
 // EDGE = false: the wave's whole tile lies inside R x C and every caller buffer
 // allows 4-element vectors, so no access needs a bounds check or a scalar tail.
-template <int TI, bool FIRST, bool LAST, bool EDGE, class M>
-__device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, int lane, int band, AxpyRaw<TI>& w) {
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI>
+__device__ __forceinline__ void axpy_load(const AxpyCtx& x, const HiCap<TI>& cap, int row0, int col0, int lane,
+                                          int band, AxpyRaw<TI>& w) {
 #pragma unroll
     for (int q = 0; q < EpiGeom<TI>::NQ; ++q) {
         int lr, lc;
@@ -981,7 +1022,9 @@ __device__ __forceinline__ void axpy_load(const AxpyCtx& x, int row0, int col0, 
         const bool vec = !EDGE || (x.vio && nv == 4);
         if (!FIRST) {   // padded buffers: in bounds
             const int64_t off = int64_t(r) * x.ldq + c;
-            const u32x2_t hi = *gm(reinterpret_cast<const u32x2_t*>(x.xhi + off));
+            u32x2_t hi;
+            if constexpr (CAPHI) hi = cap.v[band][q];
+            else hi = *gm(reinterpret_cast<const u32x2_t*>(x.xhi + off));
             const u32x2_t lo = *gm(reinterpret_cast<const u32x2_t*>(x.xlo + off));
             w.ra[q] = u32x4_t{hi[0], hi[1], lo[0], lo[1]};
         } else {
@@ -1069,24 +1112,24 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
     }
 }
 
-template <int TI, bool FIRST, bool LAST, bool EDGE, class M>
-__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const f32x4_t (&acc)[TI][TI], int row0, int col0,
-                                              int lane, float* __restrict__ stg) {
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI>
+__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>& cap, const f32x4_t (&acc)[TI][TI],
+                                              int row0, int col0, int lane, float* __restrict__ stg) {
     AxpyRaw<TI> w[2];
-    axpy_load<TI, FIRST, LAST, EDGE, M>(x, row0, col0, lane, 0, w[0]);
+    axpy_load<TI, FIRST, LAST, EDGE, M, CAPHI>(x, cap, row0, col0, lane, 0, w[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i + 1 < TI)   // one band ahead
-            axpy_load<TI, FIRST, LAST, EDGE, M>(x, row0, col0, lane, i + 1, w[(i + 1) & 1]);
+            axpy_load<TI, FIRST, LAST, EDGE, M, CAPHI>(x, cap, row0, col0, lane, i + 1, w[(i + 1) & 1]);
         stage_band<TI>(stg, acc, i, lane);
         axpy_store<TI, FIRST, LAST, EDGE, M>(x, stg, row0, col0, lane, i, w[i & 1]);
     });
 }
 
-template <int TI, bool FIRST, bool LAST>
+template <int TI, bool FIRST, bool LAST, bool CAPHI>
 __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                         const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                         float* __restrict__ stg) {
+                                         const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap, int row0, int col0,
+                                         int lane, float* __restrict__ stg) {
     AxpyCtx x;
     const int it = pa.iter;
     x.xhi = reinterpret_cast<const uint16_t*>(pa.ws + (((it - 2) & 1) ? md.off_xb1 : md.off_xb0));   // it >= 2
@@ -1104,22 +1147,22 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
     x.io = io_view(md, pa.nesterov != 0);
     constexpr int WT = EpiGeom<TI>::WT;
     if (!(x.vio && row0 + WT <= x.R && col0 + WT <= x.C)) {
-        epi_axpy_body<TI, FIRST, LAST, true, IoRuntime>(x, acc, row0, col0, lane, stg);
+        epi_axpy_body<TI, FIRST, LAST, true, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
         return;
     }
     // interior: pick the caller-buffer configuration at compile time
     const IoView& v = x.io;
     if constexpr (FIRST == LAST) {   // middle iterations read no caller buffer; both at once (one iteration) stays generic
-        epi_axpy_body<TI, FIRST, LAST, false, IoRuntime>(x, acc, row0, col0, lane, stg);
+        epi_axpy_body<TI, FIRST, LAST, false, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
     } else if constexpr (FIRST) {
         auto go = [&](auto dtc) __attribute__((always_inline)) {
             constexpr int D = decltype(dtc)::value;
             if (v.has_mom && !v.nest)
-                epi_axpy_body<TI, true, false, false, IoFixed<D, true, false, false, false>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, false, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
             else if (v.has_mom)
-                epi_axpy_body<TI, true, false, false, IoFixed<D, true, true, false, false>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, true, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
             else
-                epi_axpy_body<TI, true, false, false, IoFixed<D, false, false, false, false>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, false, false, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
         };
         if (v.dt == 0) go(std::integral_constant<int, 0>{});
         else go(std::integral_constant<int, 1>{});
@@ -1127,13 +1170,13 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
         auto go = [&](auto dtc) __attribute__((always_inline)) {
             constexpr int D = decltype(dtc)::value;
             if (v.has_param && !v.upd)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, false>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
             else if (v.has_param)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, true>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, true>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
             else if (v.upd)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, false, true>>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, false, true>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
             else
-                epi_axpy_body<TI, false, true, false, IoRuntime>(x, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
         };
         if (v.dt == 0) go(std::integral_constant<int, 0>{});
         else go(std::integral_constant<int, 1>{});
@@ -1261,14 +1304,14 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
-template <int KIND, int TI, bool FIRST>
+template <int KIND, int TI, bool FIRST, bool CAPHI = false>
 __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                                const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                                char* __restrict__ wlds) {
+                                                const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap, int row0,
+                                                int col0, int lane, char* __restrict__ wlds) {
     if constexpr (KIND == PH_AXPY)
-        epi_axpy<TI, FIRST, false>(md, t, pa, acc, row0, col0, lane, reinterpret_cast<float*>(wlds));
+        epi_axpy<TI, FIRST, false, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, reinterpret_cast<float*>(wlds));
     else if constexpr (KIND == PH_AXPY_LAST)
-        epi_axpy<TI, FIRST, true>(md, t, pa, acc, row0, col0, lane, reinterpret_cast<float*>(wlds));
+        epi_axpy<TI, FIRST, true, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, reinterpret_cast<float*>(wlds));
     else
         epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, wlds);
 }
@@ -1305,13 +1348,21 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 #pragma unroll
         for (int j = 0; j < TI; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    HiCap<TI> cap;
     if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
-        if (op.a_kc && op.b_kc)
-            mainloop<BM, kBK, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
-        else
-            mainloop<BM, kBK, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        // 128-wide tiles after the first iteration keep the bf16 X of their own
+        // quadrant from the operand stream (see HiCap)
+        constexpr bool CAPHI = !FIRST && BM == 128 && WT == kBK;
+        if (op.a_kc && op.b_kc) {   // transposed matrix: X^T B, X is the A operand
+            cap.kb = (row_b0 + wc) / kBK;
+            mainloop<BM, kBK, true, true, false, CAPHI ? 2 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+        } else {                    // B X, X is the B operand
+            cap.kb = (row_a0 + wr) / kBK;
+            mainloop<BM, kBK, true, false, false, CAPHI ? 1 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+        }
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_AXPY_BYTES);
+        epilogue_staged<KIND, TI, FIRST, CAPHI>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane,
+                                                smem + wave * EPI_AXPY_BYTES);
     } else {
         // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
         if (KIND == PH_POLY || (op.a_kc && op.b_kc))
@@ -1319,7 +1370,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
         else
             mainloop<BM, kBK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
+        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
     }
 }
 
