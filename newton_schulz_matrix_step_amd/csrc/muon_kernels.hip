@@ -3,12 +3,13 @@
 //  momentum_kernel      m' = beta m + g, u = g + beta m' (Nesterov) or m',
 //                       operand copy of u, per-unit sum of u^2      (HBM bound)
 //  finalize_norm        1 / (||u||_F + eps) per matrix, fixed-order sum
-//  ns_gemm_kernel<KIND> the three products of one quintic Newton-Schulz
+//  ns_gemm_bf16<KIND>   the three products of one quintic Newton-Schulz
 //                       iteration, grouped over every matrix of the call:
 //                         GRAM  A = X X^T           (upper tiles, mirrored store)
 //                         POLY  B = b A + c A A     (A symmetric: A A = A A^T)
-//                         AXPY  X' = a X + B X      (fp32 master + operand copy)
+//                         AXPY  X' = a X + B X      (master X as bf16 hi + lo)
 //                         AXPY_LAST  same, then W' = W (1 - lr wd) - lr s O
+//  ns_gemm_kernel<KIND> the same phases in fp32 (validation mode)
 //  direct_update        the update when ns_steps == 0
 //
 // The iteration follows the Newton-Schulz routine of the "NanoGPT Speedrun"
@@ -16,9 +17,7 @@
 // follow "14 -- modded-nanogpt", section 3 pseudocode.
 //
 // MFMA products: v_mfma_f32_16x16x32_bf16 (bf16 mode) or v_mfma_f32_16x16x4_f32
-// (fp32 validation mode), fp32 accumulation.  Both operands are staged in LDS
-// as [row][k] in 16-byte chunks, XOR-swizzled; an operand whose k index is the
-// row index in memory is transposed in registers on its way to LDS.
+// (fp32 validation mode), fp32 accumulation.
 
 #include <hip/hip_ext.h>
 
@@ -574,17 +573,16 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
 
 // ---------------------------------------------------------------------------
 // bf16 GEMM: BM x BM tiles (BM = 256 or 128), 4 waves of (BM/2)^2 outputs each,
-// k blocks of 32 through a ring of 4 LDS stages, loads issued 3 blocks ahead.
+// k blocks of 64 through a ring of LDS stages (two at both tile sizes).
 //
 // Global -> LDS uses direct-to-LDS 16-byte loads (no staging registers),
-// issued from inline asm with explicit vmcnt waits: every stage is waited for
-// exactly when it is consumed, so three blocks of loads stay in flight behind
-// the MFMAs.  Row-contiguous operands sit in LDS as [row][4 chunks of 8 k]
-// (chunk XOR (row >> 1) & 3) and feed the MFMA with ds_read_b128; k-strided
-// operands sit as [k][BM] (chunk XOR 2 (k & 7)) and feed it with
-// ds_read_b64_tr_b16, which hands lane j of each 16-lane group column j of a
-// 4 x 16 block.  Operand layouts are template parameters so the k loop is
-// straight-line code.
+// issued from inline asm with explicit vmcnt waits, so each stage is waited
+// for exactly when it is consumed.  Row-contiguous operands sit in LDS as
+// [row][8 chunks of 8 k] (chunk XOR row & 7) and feed the MFMA with
+// ds_read_b128; k-strided operands sit as [k][BM] (chunks swizzled by kswz) and
+// feed it with ds_read_b64_tr_b16, which hands lane j of each 16-lane group
+// column j of a 4 x 16 block.  Operand layouts are template parameters so the
+// k loop is straight-line code.
 // ---------------------------------------------------------------------------
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 #ifndef LDS_AS
