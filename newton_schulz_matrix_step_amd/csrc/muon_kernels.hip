@@ -748,7 +748,8 @@ __device__ __forceinline__ void row_run(int q, int lane, int& lr, int& lc) {
 // run order (band i, run q: row 16 i + lr, columns lc..lc+3), so the epilogue
 // does not read it again from HBM.  CAP 1: X is the k-strided B operand
 // ([k][BM], quadrant rows = k); CAP 2: X is the row-contiguous A operand
-// ([row][k], quadrant columns = k).
+// ([row][k], quadrant columns = k).  CAP 3: the same for POLY's own A operand
+// (A (r, c) for its b A term), in the swapped accumulator layout.
 template <int TI>
 struct HiCap {
     static constexpr int N = TI * 16 == 64 ? TI : 1;   // only quadrants of one 64-deep k block capture
@@ -769,8 +770,11 @@ __device__ __forceinline__ void capture_hi(const char* __restrict__ st, HiCap<TI
             if constexpr (CAP == 1) {
                 const int k = 16 * i + lr, n = wc + lc;
                 off = C::OPB + k * (BM * 2) + (((n >> 3) ^ kswz(k)) << 4) + (n & 7) * 2;
-            } else {
+            } else if constexpr (CAP == 2) {
                 const int r = wr + 16 * i + lr, k = lc;
+                off = r * (C::CPK * 16) + (((k >> 3) ^ kcswz<C::CPK>(r)) << 4) + (k & 7) * 2;
+            } else {   // CAP 3: swapped accumulator layout (row 16 i + (lane & 15), columns 16 q + 4 (lane >> 4) ..)
+                const int r = wr + 16 * i + (lane & 15), k = 16 * q + 4 * (lane >> 4);
                 off = r * (C::CPK * 16) + (((k >> 3) ^ kcswz<C::CPK>(r)) << 4) + (k & 7) * 2;
             }
             cap.v[i][q] = *reinterpret_cast<const u32x2_t*>(st + off);
@@ -1240,10 +1244,10 @@ __device__ __forceinline__ void sym_mirror(const SymCtx& x, const uint16_t* __re
     }
 }
 
-template <int KIND, int TI>
+template <int KIND, int TI, bool CAPA>
 __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                        const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
-                                        char* __restrict__ wlds) {
+                                        const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap, int row0, int col0,
+                                        int lane, char* __restrict__ wlds) {
     constexpr bool POLY = KIND == PH_POLY;
     uint16_t* tt = reinterpret_cast<uint16_t*>(wlds);
     SymCtx x;
@@ -1266,9 +1270,12 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < TI; ++j)
-                av[i][j] = *gm(reinterpret_cast<const u32x2_t*>(x.ain + int64_t(row0 + 16 * i + l16) * x.ldq + col0 +
-                                                                16 * j + g4));
+            for (int j = 0; j < TI; ++j) {
+                if constexpr (CAPA) av[i][j] = cap.v[i][j];   // kept from the operand stream
+                else
+                    av[i][j] = *gm(reinterpret_cast<const u32x2_t*>(x.ain + int64_t(row0 + 16 * i + l16) * x.ldq +
+                                                                    col0 + 16 * j + g4));
+            }
     }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -1311,7 +1318,7 @@ __device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t
     else if constexpr (KIND == PH_AXPY_LAST)
         epi_axpy<TI, FIRST, true, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, reinterpret_cast<float*>(wlds));
     else
-        epi_sym<KIND, TI>(md, t, pa, acc, row0, col0, lane, wlds);
+        epi_sym<KIND, TI, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, wlds);
 }
 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
@@ -1362,13 +1369,20 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
         epilogue_staged<KIND, TI, FIRST, CAPHI>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane,
                                                 smem + wave * EPI_AXPY_BYTES);
     } else {
-        // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
-        if (KIND == PH_POLY || (op.a_kc && op.b_kc))
+        // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc),
+        // keeping A (r, c) of its quadrant for the b A term (see HiCap)
+        constexpr bool CAPA = KIND == PH_POLY && WT == kBK;
+        if constexpr (KIND == PH_POLY) {
+            cap.kb = (row_b0 + wc) / kBK;
+            mainloop<BM, kBK, true, true, true, CAPA ? 3 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+        } else if (op.a_kc && op.b_kc) {
             mainloop<BM, kBK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
-        else
+        } else {
             mainloop<BM, kBK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+        }
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
+        epilogue_staged<KIND, TI, FIRST, CAPA>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane,
+                                               smem + wave * EPI_SYM_BYTES);
     }
 }
 
