@@ -784,10 +784,16 @@ __device__ __forceinline__ void capture_hi(const char* __restrict__ st, HiCap<TI
 
 // SWAP: feed the MFMA (B fragment, A fragment), so each lane accumulates 4
 // consecutive output columns of one row instead of 4 rows of one column.
-template <int BM, int BK, bool AKC, bool BKC, bool SWAP, int CAP = 0>
+struct NoPre {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// pre(): called once, at the start of the last k block (after its operands
+// landed), so an epilogue can issue its first global loads behind the last MFMAs.
+template <int BM, int BK, bool AKC, bool BKC, bool SWAP, int CAP = 0, class Pre = NoPre>
 __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0, int wave,
                                          int lane, f32x4_t (&acc)[BfCfg<BM, BK>::TI][BfCfg<BM, BK>::TI],
-                                         HiCap<BfCfg<BM, BK>::TI>* cap = nullptr) {
+                                         HiCap<BfCfg<BM, BK>::TI>* cap = nullptr, const Pre& pre = Pre()) {
     using C = BfCfg<BM, BK>;
     constexpr int TI = C::TI;
     const int wr = (wave >> 1) * C::WT, wc = (wave & 1) * C::WT;
@@ -812,6 +818,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
         const char* sb = sa + C::OPB;
         if constexpr (CAP != 0)
             if (kb == cap->kb) capture_hi<BM, BK, CAP, TI>(sa, *cap, wr, wc, lane);
+        if constexpr (!std::is_same_v<Pre, NoPre>)
+            if (kb == nk - 1) pre();
 #pragma unroll
         for (int s = 0; s < BK / 32; ++s) {
             bf16x8_t fa[TI], fb[TI];
@@ -1114,11 +1122,13 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
     }
 }
 
-template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI>
-__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>& cap, const f32x4_t (&acc)[TI][TI],
-                                              int row0, int col0, int lane, float* __restrict__ stg) {
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI, bool PRE>
+__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>& cap, const AxpyRaw<TI>& w0,
+                                              const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
+                                              float* __restrict__ stg) {
     AxpyRaw<TI> w[2];
-    axpy_load<TI, FIRST, LAST, EDGE, M, CAPHI>(x, cap, row0, col0, lane, 0, w[0]);
+    if constexpr (PRE) w[0] = w0;
+    else axpy_load<TI, FIRST, LAST, EDGE, M, CAPHI>(x, cap, row0, col0, lane, 0, w[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i + 1 < TI)   // one band ahead
@@ -1128,10 +1138,8 @@ __device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>&
     });
 }
 
-template <int TI, bool FIRST, bool LAST, bool CAPHI>
-__device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                         const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap, int row0, int col0,
-                                         int lane, float* __restrict__ stg) {
+template <bool FIRST>
+__device__ __forceinline__ AxpyCtx axpy_ctx(const MatDesc& md, const Tile& t, const PhaseArgs& pa) {
     AxpyCtx x;
     const int it = pa.iter;
     x.xhi = reinterpret_cast<const uint16_t*>(pa.ws + (((it - 2) & 1) ? md.off_xb1 : md.off_xb0));   // it >= 2
@@ -1147,24 +1155,32 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
     x.wdec = 1.f - pa.lr * pa.wd;
     x.step = pa.lr * md.shape_scale;
     x.io = io_view(md, pa.nesterov != 0);
+    return x;
+}
+
+// PRE: band 0's raw operands were loaded during the last k block (w0).
+template <int TI, bool FIRST, bool LAST, bool CAPHI, bool PRE>
+__device__ __forceinline__ void epi_axpy(const AxpyCtx& x, const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap,
+                                         const AxpyRaw<TI>& w0, int row0, int col0, int lane,
+                                         float* __restrict__ stg) {
     constexpr int WT = EpiGeom<TI>::WT;
     if (!(x.vio && row0 + WT <= x.R && col0 + WT <= x.C)) {
-        epi_axpy_body<TI, FIRST, LAST, true, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+        epi_axpy_body<TI, FIRST, LAST, true, IoRuntime, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
         return;
     }
     // interior: pick the caller-buffer configuration at compile time
     const IoView& v = x.io;
     if constexpr (FIRST == LAST) {   // middle iterations read no caller buffer; both at once (one iteration) stays generic
-        epi_axpy_body<TI, FIRST, LAST, false, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+        epi_axpy_body<TI, FIRST, LAST, false, IoRuntime, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
     } else if constexpr (FIRST) {
         auto go = [&](auto dtc) __attribute__((always_inline)) {
             constexpr int D = decltype(dtc)::value;
             if (v.has_mom && !v.nest)
-                epi_axpy_body<TI, true, false, false, IoFixed<D, true, false, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, false, false, false>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
             else if (v.has_mom)
-                epi_axpy_body<TI, true, false, false, IoFixed<D, true, true, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, true, true, false, false>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
             else
-                epi_axpy_body<TI, true, false, false, IoFixed<D, false, false, false, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, true, false, false, IoFixed<D, false, false, false, false>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
         };
         if (v.dt == 0) go(std::integral_constant<int, 0>{});
         else go(std::integral_constant<int, 1>{});
@@ -1172,13 +1188,13 @@ __device__ __forceinline__ void epi_axpy(const MatDesc& md, const Tile& t, const
         auto go = [&](auto dtc) __attribute__((always_inline)) {
             constexpr int D = decltype(dtc)::value;
             if (v.has_param && !v.upd)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, false>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, false>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
             else if (v.has_param)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, true>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, true, true>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
             else if (v.upd)
-                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, false, true>, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoFixed<D, false, false, false, true>, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
             else
-                epi_axpy_body<TI, false, true, false, IoRuntime, CAPHI>(x, cap, acc, row0, col0, lane, stg);
+                epi_axpy_body<TI, false, true, false, IoRuntime, CAPHI, PRE>(x, cap, w0, acc, row0, col0, lane, stg);
         };
         if (v.dt == 0) go(std::integral_constant<int, 0>{});
         else go(std::integral_constant<int, 1>{});
@@ -1309,18 +1325,6 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
-template <int KIND, int TI, bool FIRST, bool CAPHI = false>
-__device__ __forceinline__ void epilogue_staged(const MatDesc& md, const Tile& t, const PhaseArgs& pa,
-                                                const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap, int row0,
-                                                int col0, int lane, char* __restrict__ wlds) {
-    if constexpr (KIND == PH_AXPY)
-        epi_axpy<TI, FIRST, false, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, reinterpret_cast<float*>(wlds));
-    else if constexpr (KIND == PH_AXPY_LAST)
-        epi_axpy<TI, FIRST, true, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, reinterpret_cast<float*>(wlds));
-    else
-        epi_sym<KIND, TI, CAPHI>(md, t, pa, acc, cap, row0, col0, lane, wlds);
-}
-
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
@@ -1355,19 +1359,37 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
 
     HiCap<TI> cap;
     if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+        constexpr bool LAST = KIND == PH_AXPY_LAST;
         // 128-wide tiles after the first iteration keep the bf16 X of their own
-        // quadrant from the operand stream (see HiCap)
+        // quadrant from the operand stream (see HiCap), and all but the last
+        // iteration issue the epilogue's first band of loads during the last
+        // k block
         constexpr bool CAPHI = !FIRST && BM == 128 && WT == kBK;
+        constexpr bool PRE = BM == 128 && !LAST;   // (measured slower on the last iteration)
+        const AxpyCtx x = axpy_ctx<FIRST>(md, t, pa);
+        AxpyRaw<TI> w0;
+        const int er0 = row_a0 + wr, ec0 = row_b0 + wc;
+        auto pre = [&]() __attribute__((always_inline)) {
+            axpy_load<TI, FIRST, LAST, true, IoRuntime, CAPHI>(x, cap, er0, ec0, lane, 0, w0);
+        };
+        auto run = [&](auto capc, auto akc) __attribute__((always_inline)) {
+            constexpr int CAPV = decltype(capc)::value;
+            constexpr bool AKC_ALL = decltype(akc)::value;
+            if constexpr (PRE)
+                mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap, pre);
+            else
+                mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+        };
         if (op.a_kc && op.b_kc) {   // transposed matrix: X^T B, X is the A operand
             cap.kb = (row_b0 + wc) / kBK;
-            mainloop<BM, kBK, true, true, false, CAPHI ? 2 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+            run(std::integral_constant<int, CAPHI ? 2 : 0>{}, std::true_type{});
         } else {                    // B X, X is the B operand
             cap.kb = (row_a0 + wr) / kBK;
-            mainloop<BM, kBK, true, false, false, CAPHI ? 1 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+            run(std::integral_constant<int, CAPHI ? 1 : 0>{}, std::false_type{});
         }
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST, CAPHI>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane,
-                                                smem + wave * EPI_AXPY_BYTES);
+        epi_axpy<TI, FIRST, LAST, CAPHI, PRE>(x, acc, cap, w0, er0, ec0, lane,
+                                              reinterpret_cast<float*>(smem + wave * EPI_AXPY_BYTES));
     } else {
         // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc),
         // keeping A (r, c) of its quadrant for the b A term (see HiCap)
@@ -1381,8 +1403,7 @@ __global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restri
             mainloop<BM, kBK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         }
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-        epilogue_staged<KIND, TI, FIRST, CAPA>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane,
-                                               smem + wave * EPI_SYM_BYTES);
+        epi_sym<KIND, TI, CAPA>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
     }
 }
 
