@@ -41,13 +41,7 @@ constexpr int kMaxNsSteps = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
-#ifndef MUON_LARGE_TILE_MIN_TILES
-#define MUON_LARGE_TILE_MIN_TILES 512   // large AXPY tiles only with at least this many of them
-#endif
-#ifndef MUON_LONG_K
-#define MUON_LONG_K 3072                // AXPY k (= m) from which 256-wide tiles pay off
-#endif
-constexpr int kLongK = MUON_LONG_K;
+
 
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -252,29 +246,14 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         geom[i] = d;
     }
 
-    // Newton-Schulz tile lists.  One tile edge per phase for the whole call.
-    // GRAM/POLY (upper triangle of the m x m product): 128-wide tiles, two
-    // workgroups per CU, so one tile's mirrored epilogue overlaps another's
-    // main loop (measured faster than 256-wide tiles at every workload size).
-    // AXPY (the stored R x C shape; X is kept in the caller's orientation,
-    // transposed matrices as X^T; k = m): 256-wide tiles, which halve the
-    // operand traffic per flop, pay off once most of the flops sit in long-k
-    // matrices (m >= 3072 here) and the phase still has a couple of tiles per
-    // CU; with shorter k the 128-wide tiles win, their epilogues overlapping
-    // the other workgroup's main loop.
-    int gram_tile = kTileF32, axpy_tile = kTileF32;
-    if (!f32c) {
-        gram_tile = kTileSmall;
-        double flops = 0, long_k = 0;
-        int64_t large_tiles = 0;
-        for (const MatDesc& d : geom) {
-            const double f = double(d.m) * d.m * d.n;
-            flops += f;
-            if (d.m >= kLongK) long_k += f;
-            large_tiles += int64_t((d.R + kTileLarge - 1) / kTileLarge) * ((d.C + kTileLarge - 1) / kTileLarge);
-        }
-        axpy_tile = (2 * long_k > flops && large_tiles >= MUON_LARGE_TILE_MIN_TILES) ? kTileLarge : kTileSmall;
-    }
+    // Newton-Schulz tile edge: 128 x 128 in bf16 mode for every phase.  Two
+    // workgroups share a CU, so one tile's epilogue overlaps another's main
+    // loop; AXPY tiles of this size also keep their quadrant of X from the
+    // operand stream.  256-wide tiles (one workgroup per CU, half the operand
+    // traffic per flop) measured slower on every workload once those
+    // epilogue savings were in.
+    const int gram_tile = f32c ? kTileF32 : kTileBf16;
+    const int axpy_tile = gram_tile;
     // Tile lists.  Workgroup b runs on XCD b % 8, and each XCD has its own L2,
     // so every list is 8 chunks, one per XCD: chunk x holds the tiles XCD x
     // runs, in dispatch order.  Tiles come in items (one matrix's group of up

@@ -10,7 +10,7 @@ namespace muon {
 // All workspace matrices are padded to multiples of this many rows/columns and
 // zero-filled once, so tile loads never leave the allocation and padding reads
 // contribute zeros to every contraction.
-constexpr int kPad = 256;
+constexpr int kPad = 128;
 
 // Per-matrix descriptor, one entry per matrix of the call, in device memory.
 // "Stored" = the caller's orientation (R x C); "NS" = the m x n orientation the
@@ -83,11 +83,8 @@ hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* til
 hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats,
                                 PhaseArgs a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
-// Tile edges of the Newton-Schulz GEMMs: fp32 mode uses kTileF32; bf16 mode
-// uses kTileSmall for GRAM/POLY and kTileLarge or kTileSmall for AXPY from
-// the tile count.
+// Tile edge of the Newton-Schulz GEMMs (both modes use 128 x 128 tiles).
 constexpr int kTileF32 = 128;
-constexpr int kTileLarge = 256;
-constexpr int kTileSmall = 128;
+constexpr int kTileBf16 = 128;
 
 }  // namespace muon

@@ -572,8 +572,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const Tile* __restric
 }
 
 // ---------------------------------------------------------------------------
-// bf16 GEMM: BM x BM tiles (BM = 256 or 128), 4 waves of (BM/2)^2 outputs each,
-// k blocks of 64 through a ring of LDS stages (two at both tile sizes).
+// bf16 GEMM: BM x BM tiles (BM = 128), 4 waves of (BM/2)^2 outputs each, k
+// blocks of 64 through a ring of two LDS stages (64 KB: two workgroups per CU).
 //
 // Global -> LDS uses direct-to-LDS 16-byte loads (no staging registers),
 // issued from inline asm with explicit vmcnt waits, so each stage is waited
@@ -592,10 +592,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int BM, int BK_ = 64>
 struct BfCfg {
     static constexpr int BK = BK_;                // k per LDS stage (32 or 64)
-    // LDS stages (ring; the epilogue reuses them): 256-wide tiles take the whole
-    // 160 KB (one workgroup per CU), 128-wide tiles stay within 64 KB so two
+    // LDS stages (ring; the epilogue reuses them), within 64 KB so two
     // workgroups share a CU
-    static constexpr int LDS_BUDGET = BM == 256 ? 160 * 1024 : 64 * 1024;
+    static constexpr int LDS_BUDGET = 64 * 1024;
     static constexpr int NST = LDS_BUDGET / (2 * BM * BK * 2) > 8 ? 8 : LDS_BUDGET / (2 * BM * BK * 2);
     static constexpr int CPK = BK / 8;            // 16-byte chunks per [row][BK] row
     static constexpr int WT = BM / 2;             // wave tile edge
@@ -1488,20 +1487,13 @@ static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, con
                               mats, a);
         return;
     }
-    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
-        if (tile == 256) {
-            launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
-            return;
-        }
-    }
     launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    const bool axpy = kind == PH_AXPY || kind == PH_AXPY_LAST;
-    if (tile != 128 && !(tile == 256 && axpy && !f32c)) return hipErrorInvalidValue;
+    if (tile != 128) return hipErrorInvalidValue;
     switch (kind) {
         case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
