@@ -1327,7 +1327,7 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
-__global__ __launch_bounds__(kThreads, 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
+__global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restrict__ tiles,
                                                             const MatDesc* __restrict__ mats, PhaseArgs pa,
                                                             int n_tiles) {
     using C = BfCfg<BM, kBK>;
