@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void finalize_norm_kernel(const MatDesc* 
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if (int(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x == 0) {
@@ -841,25 +841,8 @@ __device__ __forceinline__ void mainloop(char* __restrict__ smem, const Operands
 }
 
 
-__device__ __forceinline__ f32x4_t ld4_bf16(const void* p) {
-    const u32x2_t w = *gm(reinterpret_cast<const u32x2_t*>(p));
-    return f32x4_t{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
-                   __uint_as_float(w[1] & 0xFFFF0000u)};
-}
 __device__ __forceinline__ void st4_bf16(void* p, f32x4_t v) {
     *gm(reinterpret_cast<u32x2_t*>(p)) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-}
-// 4 consecutive elements of a caller buffer (dtype 0 bf16 / 1 f32); `vec`: aligned and in range
-__device__ __forceinline__ f32x4_t ld4_io(const void* p, int64_t i, int dt, bool vec, int nvalid) {
-    if (vec) {
-        if (dt == 0) return ld4_bf16(static_cast<const uint16_t*>(p) + i);
-        return *gm(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i));
-    }
-    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (q < nvalid) v[q] = load_elem(p, i + q, dt);
-    return v;
 }
 __device__ __forceinline__ void st4_io(void* p, int64_t i, int dt, bool vec, int nvalid, f32x4_t v) {
     if (vec) {
@@ -904,19 +887,6 @@ __device__ __forceinline__ IoView io_view(const MatDesc& md, bool nest) {
     v.nest = nest;
     v.vio = md.vec_io != 0;
     return v;
-}
-
-// u at 4 consecutive stored elements (r, c..c+3): m' (or g without momentum),
-// g + beta m' with Nesterov; only the buffers the form needs are read
-__device__ __forceinline__ f32x4_t u4_at(const IoView& v, int64_t r, int64_t c, float beta, bool vec, int nvalid) {
-    if (!v.has_mom) return ld4_io(v.grad, r * v.ld_grad + c, v.dt, vec, nvalid);
-    const f32x4_t mn = ld4_io(v.mom, r * v.ld_mom + c, 1, vec, nvalid);
-    if (!v.nest) return mn;
-    const f32x4_t g = ld4_io(v.grad, r * v.ld_grad + c, v.dt, vec, nvalid);
-    f32x4_t u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) u[q] = fmaf(beta, mn[q], g[q]);
-    return u;
 }
 
 // Epilogue through LDS.  Each wave stages its (16 x WT) row bands in fp32 in its
@@ -986,8 +956,6 @@ __device__ __forceinline__ f32x4_t dec4(u32x4_t r, int dt) {
 // fast path, where it removes every per-run branch on dtype and buffer presence.
 struct IoRuntime {
     static constexpr bool fixed = false;
-    static constexpr int dt = 0;
-    static constexpr bool mom = false, nest = false, param = false, upd = false;
 };
 template <int DT, bool MOM, bool NEST, bool PARAM, bool UPD>
 struct IoFixed {
@@ -1480,8 +1448,8 @@ static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDes
 }
 
 template <int KIND>
-static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
-                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+static void launch_kind(bool f32c, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s,
+                        hipEvent_t ev0, hipEvent_t ev1) {
     if (f32c) {
         hipExtLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0, tiles,
                               mats, a);
@@ -1495,10 +1463,10 @@ hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int
     if (n_tiles <= 0) return hipSuccess;
     if (tile != 128) return hipErrorInvalidValue;
     switch (kind) {
-        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_POLY: launch_kind<PH_POLY>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
