@@ -37,7 +37,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass
-from typing import List, Sequence, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -60,6 +60,9 @@ class Hyper:
     a: float = NS_A
     b: float = NS_B
     c: float = NS_C
+    # optional per-iteration coefficients ((a_1, b_1, c_1), ...), one triple per
+    # iteration, replacing (a, b, c) in that iteration's products
+    coeffs: Optional[Tuple[Tuple[float, float, float], ...]] = None
 
 
 # ----------------------------------------------------------------------------
@@ -98,20 +101,29 @@ def frobenius_normalize(u: np.ndarray, eps: float) -> Tuple[np.ndarray, float]:
     return u / (nu + eps), nu
 
 
-def ns_iterate(x: np.ndarray, steps: int, a: float, b: float, c: float) -> np.ndarray:
+def ns_iterate(x: np.ndarray, steps: int, a: float, b: float, c: float,
+               coeffs: Optional[Sequence[Tuple[float, float, float]]] = None) -> np.ndarray:
     """Quintic Newton-Schulz iterations on x as given (no transpose, no normalisation).
 
-    Per iteration: A = X X^T; B = b A + c A A; X = a X + B X.
+    Per iteration: A = X X^T; B = b A + c A A; X = a X + B X.  With ``coeffs``,
+    iteration k (from 1) uses the k-th triple instead of (a, b, c): the
+    per-iteration schedules the record list of the "NanoGPT Speedrun" page
+    names (Polar Express); the pages print no schedule, so the triples are
+    inputs.
     """
-    for _ in range(steps):
+    if coeffs is not None and len(coeffs) < steps:
+        raise ValueError("one coefficient triple per iteration")
+    for k in range(steps):
+        ak, bk, ck = coeffs[k] if coeffs is not None else (a, b, c)
         gram = x @ x.T
-        poly = b * gram + c * (gram @ gram)
-        x = a * x + poly @ x
+        poly = bk * gram + ck * (gram @ gram)
+        x = ak * x + poly @ x
     return x
 
 
 def newton_schulz(g: np.ndarray, steps: int = NS_STEPS, eps: float = NS_EPS,
-                  a: float = NS_A, b: float = NS_B, c: float = NS_C) -> np.ndarray:
+                  a: float = NS_A, b: float = NS_B, c: float = NS_C,
+                  coeffs: Optional[Sequence[Tuple[float, float, float]]] = None) -> np.ndarray:
     """Approximate U V^T of g's SVD ("NanoGPT Speedrun" page, Muon section).
 
     Normalise by the Frobenius norm, transpose when rows > cols (strictly), run
@@ -124,7 +136,7 @@ def newton_schulz(g: np.ndarray, steps: int = NS_STEPS, eps: float = NS_EPS,
     tall = g.shape[0] > g.shape[1]
     if tall:
         x = x.T
-    x = ns_iterate(x, steps, a, b, c)
+    x = ns_iterate(x, steps, a, b, c, coeffs)
     if tall:
         x = x.T
     return np.ascontiguousarray(x)
@@ -157,7 +169,7 @@ def muon_step_matrix(w: np.ndarray, g: np.ndarray, m: np.ndarray, hp: Hyper) -> 
     m_new = momentum_update(m, g, hp.beta)
     u = update_direction(g, m_new, hp.beta, hp.nesterov)
     nu = float(np.sqrt(np.sum(u * u)))
-    o = newton_schulz(u, hp.ns_steps, hp.eps, hp.a, hp.b, hp.c)
+    o = newton_schulz(u, hp.ns_steps, hp.eps, hp.a, hp.b, hp.c, hp.coeffs)
     s = shape_scale(*w.shape)
     w_new = param_update(w, o, hp.lr, hp.weight_decay, s)
     return StepResult(w_new, m_new, o, nu)

@@ -319,37 +319,37 @@ def test_against_torch_optim_muon_black_box():
 # --------------------------------------------------------------------------
 
 def _mutant_iterations():
-    def dropped_c(x, s, a, b, c):
+    def dropped_c(x, s, a, b, c, coeffs=None):
         for _ in range(s):
             g = x @ x.T
             x = a * x + (b * g) @ x
         return x
 
-    def wrong_sign_b(x, s, a, b, c):
+    def wrong_sign_b(x, s, a, b, c, coeffs=None):
         for _ in range(s):
             g = x @ x.T
             x = a * x + (-b * g + c * g @ g) @ x
         return x
 
-    def right_multiply(x, s, a, b, c):
+    def right_multiply(x, s, a, b, c, coeffs=None):
         for _ in range(s):
             g = x @ x.T
             x = a * x + x @ (b * g + c * g @ g)
         return x
 
-    def gram_transposed(x, s, a, b, c):
+    def gram_transposed(x, s, a, b, c, coeffs=None):
         for _ in range(s):
             g = x.T @ x
             x = a * x + (b * g + c * g @ g) @ x
         return x
 
-    def four_steps(x, s, a, b, c):
+    def four_steps(x, s, a, b, c, coeffs=None):
         for _ in range(s - 1):
             g = x @ x.T
             x = a * x + (b * g + c * g @ g) @ x
         return x
 
-    def swapped_a_c(x, s, a, b, c):
+    def swapped_a_c(x, s, a, b, c, coeffs=None):
         for _ in range(s):
             g = x @ x.T
             x = c * x + (b * g + a * g @ g) @ x
@@ -376,9 +376,85 @@ def test_closed_form_pin_detects_missing_transpose(monkeypatch):
     g = _inputs("gauss", 30, 12, 7)
     ref = svd_closed_form(g)
 
-    def no_transpose_back(gg, steps=5, eps=1e-7, a=A, b=B, c=C):
+    def no_transpose_back(gg, steps=5, eps=1e-7, a=A, b=B, c=C, coeffs=None):
         x, _ = muon_oracle.frobenius_normalize(gg, eps)
         return muon_oracle.ns_iterate(x.T, steps, a, b, c)
 
     bad = no_transpose_back(g)
     assert bad.shape != ref.shape or relf(bad, ref) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# per-iteration coefficients (a_k, b_k, c_k): the closed form composes the
+# scalar quintics in iteration order, phi = p_K o ... o p_1
+# --------------------------------------------------------------------------
+
+SCHEDULES = {
+    # assorted triples, each p_k(1) in the quintic's usual range
+    "mixed": ((3.4445, -4.7750, 2.0315), (2.0, -1.5, 0.5), (1.875, -1.25, 0.375), (3.0, -3.2, 1.2),
+              (1.5, -0.5, 0.0)),
+    "uniform": ((A, B, C),) * 5,
+    "identity": ((1.0, 0.0, 0.0),) * 5,
+}
+
+
+def phi_schedule(s, coeffs):
+    """Scalar polynomials p_k(x) = a_k x + b_k x^3 + c_k x^5 applied in order, by a Python loop."""
+    s = np.atleast_1d(np.asarray(s, dtype=np.float64))
+    out = np.empty_like(s)
+    for i, v in enumerate(s):
+        x = float(v)
+        for ak, bk, ck in coeffs:
+            x = ak * x + bk * x ** 3 + ck * x ** 5
+        out[i] = x
+    return out
+
+
+@pytest.mark.parametrize("name", ["mixed", "uniform"])
+@pytest.mark.parametrize("shape", [(40, 96), (96, 40), (64, 64)])
+def test_schedule_matches_composed_closed_form(name, shape):
+    coeffs = SCHEDULES[name]
+    g = _inputs("lowrank", shape[0], shape[1], 31)
+    u, s, vt = np.linalg.svd(g, full_matrices=False)
+    nu = math.sqrt(float(np.sum(g * g)))
+    expect = (u * phi_schedule(s / (nu + 1e-7), coeffs)) @ vt
+    got = newton_schulz(g, 5, 1e-7, coeffs=coeffs)
+    assert relf(got, expect) <= 1e-12
+
+
+def test_schedule_order_matters():
+    """The same triples in reverse order give the reversed composition (and a different O)."""
+    coeffs = SCHEDULES["mixed"]
+    g = _inputs("gauss", 48, 80, 32)
+    u, s, vt = np.linalg.svd(g, full_matrices=False)
+    x = s / (math.sqrt(float(np.sum(g * g))) + 1e-7)
+    fwd = newton_schulz(g, 5, coeffs=coeffs)
+    rev = newton_schulz(g, 5, coeffs=tuple(reversed(coeffs)))
+    assert relf(rev, (u * phi_schedule(x, tuple(reversed(coeffs)))) @ vt) <= 1e-12
+    assert relf(fwd, rev) > 1e-3
+
+
+def test_uniform_schedule_equals_scalar_coefficients():
+    g = _inputs("heavy", 64, 96, 33)
+    np.testing.assert_allclose(newton_schulz(g, 5, coeffs=SCHEDULES["uniform"]), newton_schulz(g, 5), rtol=0, atol=0)
+
+
+def test_identity_schedule_returns_normalised_input():
+    """p(x) = x at every iteration: O is the normalised input, transposes undone."""
+    for shape in [(30, 50), (50, 30)]:
+        g = _inputs("gauss", shape[0], shape[1], 34)
+        got = newton_schulz(g, 5, 1e-7, coeffs=SCHEDULES["identity"])
+        np.testing.assert_allclose(got, g / (np.linalg.norm(g) + 1e-7), rtol=1e-15, atol=0)
+
+
+def test_schedule_in_full_step():
+    """muon_step_matrix threads the schedule through to the iteration."""
+    rng = np.random.default_rng(35)
+    w, g = rng.standard_normal((24, 40)) * 0.02, rng.standard_normal((24, 40)) * 0.02
+    hp = Hyper(coeffs=SCHEDULES["mixed"])
+    r = muon_step_matrix(w, g, np.zeros_like(g), hp)
+    u, s, vt = np.linalg.svd(g, full_matrices=False)
+    o = (u * phi_schedule(s / (np.linalg.norm(g) + 1e-7), SCHEDULES["mixed"])) @ vt
+    assert relf(r.o, o) <= 1e-12
+    with pytest.raises(ValueError):
+        newton_schulz(g, 5, coeffs=SCHEDULES["mixed"][:3])
