@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -90,6 +90,11 @@ typedef struct muon_hparams {
     int32_t nesterov;          /* 0 or 1 */
     int32_t ns_steps;          /* 0..64; 5 on the pages */
     int32_t compute;           /* muon_compute */
+    const float *coeffs;       /* optional host array of ns_steps triples (a_k, b_k, c_k), iteration k
+                                  using the k-th in place of (a, b, c): per-iteration schedules such as
+                                  Polar Express, named in the record list of "NanoGPT Speedrun"
+                                  (modded-nanogpt README mirror); each finite, a_k != 0.  Read during
+                                  the call only.  NULL = (a, b, c) for every iteration. */
 } muon_hparams;
 
 typedef struct muon_handle muon_handle;
@@ -117,7 +122,8 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
  * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
  * momentum aliasing param or grad, ns_steps outside 0..64, a == 0 or a non-finite
- * coefficient, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
+ * coefficient, also in coeffs, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM,
+ * MUON_ERR_HIP. */
 muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
                       const muon_hparams *hp, void *stream);
 

@@ -190,6 +190,7 @@ class Workload:
     a: float = 3.4445
     b: float = -4.7750
     c: float = 2.0315
+    coeffs: Optional[Tuple[Tuple[float, float, float], ...]] = None   # per-iteration triples, None = (a, b, c)
     expert_scale_range: Tuple[float, float] = (-4.0, -1.0)
     description: str = ""
 

@@ -74,6 +74,7 @@ class muon_hparams(ctypes.Structure):
         ("nesterov", ctypes.c_int32),
         ("ns_steps", ctypes.c_int32),
         ("compute", ctypes.c_int32),
+        ("coeffs", ctypes.POINTER(ctypes.c_float)),
     ]
 
 
@@ -148,11 +149,20 @@ class Hparams:
     nesterov: bool = False
     ns_steps: int = 5
     compute: str = "bf16"      # "bf16" or "fp32"
+    coeffs: Optional[Sequence[Sequence[float]]] = None   # per-iteration (a_k, b_k, c_k)
 
     def to_c(self) -> muon_hparams:
         comp = {"bf16": MUON_COMPUTE_BF16, "fp32": MUON_COMPUTE_FP32}.get(self.compute, -1)
-        return muon_hparams(self.lr, self.beta, self.weight_decay, self.eps, self.a, self.b, self.c,
-                            int(bool(self.nesterov)), int(self.ns_steps), comp)
+        hp = muon_hparams(self.lr, self.beta, self.weight_decay, self.eps, self.a, self.b, self.c,
+                          int(bool(self.nesterov)), int(self.ns_steps), comp, None)
+        if self.coeffs is not None:
+            flat = [float(v) for t in self.coeffs for v in t]
+            if len(flat) != 3 * len(self.coeffs) or len(self.coeffs) < self.ns_steps:
+                raise ValueError("coeffs: one (a, b, c) triple per iteration")
+            arr = (ctypes.c_float * len(flat))(*flat)
+            hp.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+            hp._coeffs_keepalive = arr   # the array lives as long as the struct
+        return hp
 
 
 def _dtype_code(t) -> int:

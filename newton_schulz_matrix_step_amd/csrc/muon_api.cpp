@@ -164,6 +164,12 @@ muon_status validate_hp(muon_handle* h, const muon_hparams* hp) {
         return fail(h, MUON_ERR_INVALID_ARG, "ns_steps %d outside 0..%d", hp->ns_steps, kMaxNsSteps);
     if (!(std::fabs(hp->a) > 0.f) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
         return fail(h, MUON_ERR_INVALID_ARG, "coefficients must be finite with a != 0");
+    if (hp->coeffs)
+        for (int k = 0; k < hp->ns_steps; ++k) {
+            const float* t = hp->coeffs + 3 * k;
+            if (!(std::fabs(t[0]) > 0.f) || !std::isfinite(t[0]) || !std::isfinite(t[1]) || !std::isfinite(t[2]))
+                return fail(h, MUON_ERR_INVALID_ARG, "coefficient triple %d must be finite with a != 0", k + 1);
+        }
     if (hp->nesterov != 0 && hp->nesterov != 1)
         return fail(h, MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1, got %d", hp->nesterov);
     return MUON_OK;
@@ -501,6 +507,11 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
     }
     for (int it = 1; it <= hp->ns_steps; ++it) {
         pa.iter = it;
+        if (hp->coeffs) {   // this iteration's triple
+            pa.a = hp->coeffs[3 * (it - 1)];
+            pa.b = hp->coeffs[3 * (it - 1) + 1];
+            pa.c = hp->coeffs[3 * (it - 1) + 2];
+        }
         e = timed(h, K_GRAM, [&](hipEvent_t e0, hipEvent_t e1) {
             return launch_ns_phase(PH_GRAM, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream, e0, e1);
         });

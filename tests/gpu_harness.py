@@ -76,12 +76,13 @@ def weight_error_ok(w_new_bits: np.ndarray, w_old: np.ndarray, o: np.ndarray, lr
 def hparams_for(wl: Workload):
     import newton_schulz_matrix_step_amd as nsm
     return nsm.Hparams(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
-                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute)
+                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute, coeffs=wl.coeffs)
 
 
 def oracle_hyper(wl: Workload) -> oracle.Hyper:
     return oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
-                        ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c)
+                        ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
+                        coeffs=wl.coeffs)
 
 
 @dataclass

@@ -47,15 +47,16 @@ def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "muon.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(muon_matrix), sizeof(muon_hparams),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(muon_matrix), sizeof(muon_hparams),"
         " sizeof(muon_kernel_stats), offsetof(muon_matrix, dtype), offsetof(muon_hparams, ns_steps),"
-        " offsetof(muon_matrix, ld_update)); return 0;}\n")
+        " offsetof(muon_matrix, ld_update), offsetof(muon_hparams, coeffs)); return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert out == [ctypes.sizeof(_abi.muon_matrix), ctypes.sizeof(_abi.muon_hparams),
                    ctypes.sizeof(_abi.muon_kernel_stats), _abi.muon_matrix.dtype.offset,
-                   _abi.muon_hparams.ns_steps.offset, _abi.muon_matrix.ld_update.offset]
+                   _abi.muon_hparams.ns_steps.offset, _abi.muon_matrix.ld_update.offset,
+                   _abi.muon_hparams.coeffs.offset]
 
 
 def test_status_strings(lib):
@@ -92,3 +93,15 @@ def test_hparams_marshalling():
     c = nsm.Hparams(lr=0.5, nesterov=True, ns_steps=3, compute="fp32").to_c()
     assert (c.lr, c.nesterov, c.ns_steps, c.compute) == (0.5, 1, 3, nsm.MUON_COMPUTE_FP32)
     assert nsm.Hparams(compute="fp16").to_c().compute == -1
+
+
+def test_hparams_coeffs_marshalling():
+    sched = [(3.0, -3.2, 1.2), (2.5, -2.0, 0.6), (1.5, -0.5, 0.0)]
+    c = nsm.Hparams(ns_steps=3, coeffs=sched).to_c()
+    got = [c.coeffs[i] for i in range(9)]
+    assert got == pytest.approx([v for t in sched for v in t], rel=1e-7)
+    assert not nsm.Hparams().to_c().coeffs               # NULL: the default triple every iteration
+    with pytest.raises(ValueError):
+        nsm.Hparams(ns_steps=3, coeffs=sched[:2]).to_c()  # fewer triples than iterations
+    with pytest.raises(ValueError):
+        nsm.Hparams(ns_steps=1, coeffs=[(1.0, 2.0)]).to_c()

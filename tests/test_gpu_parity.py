@@ -169,3 +169,46 @@ def test_norm_readback():
         assert nu[0] == pytest.approx(float(torch.linalg.norm(g.double())), rel=1e-6)
     finally:
         nsm.muon_destroy(h)
+
+
+# per-iteration coefficient schedules: assorted triples (the first is the
+# default quintic, the last a plain cubic step) and the default one repeated
+MIXED_SCHEDULE = ((3.4445, -4.7750, 2.0315), (2.0, -1.5, 0.5), (1.875, -1.25, 0.375), (3.0, -3.2, 1.2),
+                  (1.5, -0.5, 0.0))
+
+
+@pytest.mark.parametrize("compute,tol", [("bf16", TOL_O_BF16), ("fp32", 1e-4)])
+def test_coefficient_schedule(compute, tol):
+    shapes = [(300, 100), (100, 300), (256, 256), (129, 515), (64, 64), (17, 1)]
+    wl = _wl("sched", shapes, steps=2, nesterov=True, compute=compute, coeffs=MIXED_SCHEDULE)
+    rep = []
+    rec = run_gpu(wl, 2, list(range(len(shapes))))
+    check_against_oracle(wl, rec, tol, tol_w_f32=tol, report=rep)
+    print(compute, "schedule worst O rel err", max(e for (_, _, _, e) in rep))
+
+
+def test_uniform_schedule_matches_default_bitwise():
+    wl = _wl("uni", [(300, 100), (128, 384)], steps=2)
+    a = run_gpu(wl, 2, [0, 1])
+    b = run_gpu(wl.with_(coeffs=((wl.a, wl.b, wl.c),) * wl.ns_steps), 2, [0, 1])
+    for i in (0, 1):
+        for ra, rb in zip(a[i], b[i]):
+            assert np.array_equal(ra.o, rb.o) and np.array_equal(ra.w_new, rb.w_new)
+
+
+@pytest.mark.parametrize("bad", [(0.0, -1.0, 0.5), (float("nan"), 1.0, 1.0), (1.0, float("inf"), 0.0)])
+def test_invalid_schedule_rejected(bad):
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    h = nsm.muon_init(0)
+    try:
+        g = torch.randn(40, 60, device="cuda")
+        w = torch.zeros_like(g)
+        m = torch.zeros_like(g)
+        sched = [(3.4445, -4.7750, 2.0315)] * 4 + [bad]
+        with pytest.raises(nsm.MuonError) as ei:
+            nsm.muon_step(h, [w], [g], [m], nsm.Hparams(coeffs=sched))
+        assert ei.value.status == nsm.MUON_ERR_INVALID_ARG
+        assert float(w.abs().max()) == 0.0 and float(m.abs().max()) == 0.0   # nothing ran
+    finally:
+        nsm.muon_destroy(h)
