@@ -13,12 +13,14 @@ from .muon_oracle import (  # noqa: F401
     NS_STEPS,
     Hyper,
     StepResult,
+    block_corners,
     decode,
     frobenius_normalize,
     momentum_update,
     muon_overhead_fraction,
     muon_step,
     muon_step_matrix,
+    muon_step_matrix_blocked,
     newton_schulz,
     ns_flops_dense,
     ns_flops_unique,

@@ -27,6 +27,9 @@ Readings where the pages are silent (each also listed in the design notes):
   applied to the old W.
 * Shape scale s = sqrt(max(1, rows/cols)) on the stored shape.
 * No bfloat16 cast of the normalised input: the oracle is exact float64.
+* Sub-block orthogonalisation (query/key weights in pairs of heads): each block
+  is a matrix of its own for the norm, the transpose rule, the iteration and
+  the shape scale; momentum stays elementwise over the whole weight.
 
 Every function here is checked against results fixed independently of it (the
 SVD closed form, the momentum geometric series, printed constants) by the
@@ -173,6 +176,47 @@ def muon_step_matrix(w: np.ndarray, g: np.ndarray, m: np.ndarray, hp: Hyper) -> 
     s = shape_scale(*w.shape)
     w_new = param_update(w, o, hp.lr, hp.weight_decay, s)
     return StepResult(w_new, m_new, o, nu)
+
+
+def block_corners(rows: int, cols: int, block_rows: int, block_cols: int) -> List[Tuple[int, int, int, int]]:
+    """(r0, c0, h, w) of every block of a rows x cols matrix cut into
+    block_rows x block_cols blocks, row-major; 0 means the whole dimension.
+    Each block size must divide its dimension."""
+    h = rows if block_rows == 0 else block_rows
+    w = cols if block_cols == 0 else block_cols
+    if h < 1 or w < 1 or rows % h or cols % w:
+        raise ValueError(f"block {block_rows} x {block_cols} does not tile {rows} x {cols}")
+    return [(r0, c0, h, w) for r0 in range(0, rows, h) for c0 in range(0, cols, w)]
+
+
+def muon_step_matrix_blocked(w: np.ndarray, g: np.ndarray, m: np.ndarray, hp: Hyper,
+                             block_rows: int, block_cols: int) -> StepResult:
+    """One Muon step where the weight is cut into blocks, each orthogonalised
+    as a matrix of its own.
+
+    "NanoGPT Speedrun" (modded-nanogpt README mirror), record list: the query
+    and key weights are orthogonalised in pairs of heads instead of across all
+    heads at once.  Reading: momentum is elementwise, so it is the whole
+    matrix's recurrence; normalisation (with its eps), the transpose rule, the
+    iteration and the shape scale all act on each block with its own shape.
+    ``nu`` holds the blocks' norms in row-major block order.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    m_new = momentum_update(m, g, hp.beta)
+    u = update_direction(g, m_new, hp.beta, hp.nesterov)
+    o = np.empty_like(u)
+    w_new = np.empty_like(w)
+    nus = []
+    for r0, c0, bh, bw in block_corners(*w.shape, block_rows, block_cols):
+        ub = u[r0:r0 + bh, c0:c0 + bw]
+        nus.append(float(np.sqrt(np.sum(ub * ub))))
+        ob = newton_schulz(ub, hp.ns_steps, hp.eps, hp.a, hp.b, hp.c, hp.coeffs)
+        o[r0:r0 + bh, c0:c0 + bw] = ob
+        w_new[r0:r0 + bh, c0:c0 + bw] = param_update(w[r0:r0 + bh, c0:c0 + bw], ob, hp.lr, hp.weight_decay,
+                                                     shape_scale(bh, bw))
+    return StepResult(w_new, m_new, o, np.array(nus))
 
 
 def muon_step(ws: Sequence[np.ndarray], gs: Sequence[np.ndarray], ms: Sequence[np.ndarray],

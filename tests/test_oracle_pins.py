@@ -458,3 +458,127 @@ def test_schedule_in_full_step():
     assert relf(r.o, o) <= 1e-12
     with pytest.raises(ValueError):
         newton_schulz(g, 5, coeffs=SCHEDULES["mixed"][:3])
+
+
+# --------------------------------------------------------------------------
+# sub-block orthogonalisation: each block is a matrix of its own (norm,
+# transpose rule, iteration, shape scale); momentum stays elementwise
+# --------------------------------------------------------------------------
+
+def _blocked_closed_form(u, bh, bw):
+    """Per-block SVD closed form, with the block slicing written out by index."""
+    R, Cc = u.shape
+    o = np.zeros_like(u)
+    for bi in range(R // bh):
+        for bj in range(Cc // bw):
+            rows = np.arange(bi * bh, (bi + 1) * bh)
+            cols = np.arange(bj * bw, (bj + 1) * bw)
+            blk = u[np.ix_(rows, cols)]
+            uu, s, vt = np.linalg.svd(blk, full_matrices=False)
+            o[np.ix_(rows, cols)] = (uu * phi(s / (np.linalg.norm(blk) + 1e-7))) @ vt
+    return o
+
+
+@pytest.mark.parametrize("shape,block", [((384, 96), (128, 0)),    # 6 heads of 64 rows, pairs of heads
+                                         ((96, 384), (0, 128)),    # the same cut along columns
+                                         ((192, 160), (64, 80)),   # a 3 x 2 grid of blocks
+                                         ((130, 60), (65, 0))])    # ragged block sizes, tall blocks
+def test_blocked_step_matches_per_block_closed_form(shape, block):
+    rng = np.random.default_rng(41)
+    g = _inputs("lowrank", shape[0], shape[1], 41)
+    w = rng.standard_normal(shape) * 0.02
+    hp = Hyper(lr=0.05, weight_decay=0.1)
+    r = oracle.muon_step_matrix_blocked(w, g, np.zeros_like(g), hp, *block)
+    bh = shape[0] if block[0] == 0 else block[0]
+    bw = shape[1] if block[1] == 0 else block[1]
+    o = _blocked_closed_form(g, bh, bw)
+    assert relf(r.o, o) <= 1e-12
+    s = math.sqrt(max(1.0, bh / bw))        # the block's own shape scale
+    assert relf(r.w, w * (1 - 0.05 * 0.1) - 0.05 * s * o) <= 1e-12
+    assert r.nu.shape == ((shape[0] // bh) * (shape[1] // bw),)
+    assert r.nu[0] == pytest.approx(np.linalg.norm(g[:bh, :bw]), rel=1e-14)
+
+
+def test_blocked_whole_matrix_equals_plain_step():
+    rng = np.random.default_rng(42)
+    w, g, m = (rng.standard_normal((48, 80)) for _ in range(3))
+    hp = Hyper(nesterov=True, weight_decay=0.01)
+    a = muon_step_matrix(w, g, m, hp)
+    for blk in [(0, 0), (48, 80), (48, 0), (0, 80)]:
+        b = oracle.muon_step_matrix_blocked(w, g, m, hp, *blk)
+        np.testing.assert_array_equal(a.o, b.o)
+        np.testing.assert_array_equal(a.w, b.w)
+        np.testing.assert_array_equal(a.m, b.m)
+        assert b.nu.tolist() == [a.nu]
+
+
+def test_blocked_rows_of_one_are_normalised_rows():
+    """A 1 x C block has one singular value, its norm ratio: O's row is phi_5(‖u‖/(‖u‖+eps)) u/‖u‖."""
+    g = _inputs("gauss", 7, 33, 43)
+    r = oracle.muon_step_matrix_blocked(np.zeros_like(g), g, np.zeros_like(g), Hyper(), 1, 0)
+    for i in range(7):
+        nrm = math.sqrt(sum(float(v) ** 2 for v in g[i]))
+        expect = phi([nrm / (nrm + 1e-7)])[0] * g[i] / nrm
+        np.testing.assert_allclose(r.o[i], expect, rtol=1e-12, atol=0)
+
+
+def test_blocked_columns_of_one_take_their_own_shape_scale():
+    """An R x 1 block is tall: transposed, and its shape scale is sqrt(R), not the whole weight's."""
+    g = _inputs("gauss", 9, 4, 44)
+    lr = 0.1
+    r = oracle.muon_step_matrix_blocked(np.zeros_like(g), g, np.zeros_like(g), Hyper(lr=lr), 0, 1)
+    for j in range(4):
+        col = g[:, j]
+        nrm = float(np.linalg.norm(col))
+        o = phi([nrm / (nrm + 1e-7)])[0] * col / nrm
+        np.testing.assert_allclose(r.o[:, j], o, rtol=1e-12, atol=0)
+        np.testing.assert_allclose(r.w[:, j], -lr * 3.0 * o, rtol=1e-12, atol=0)
+
+
+def test_blocked_norm_is_per_block():
+    """Scaling one block's gradient leaves every block's O unchanged (per-block
+    normalisation); a whole-matrix normalisation would change the others.
+    eps = 0 so that the normalisation is exactly scale invariant."""
+    g = _inputs("lowrank", 128, 64, 45)
+    hp = Hyper(eps=0.0)
+    base = oracle.muon_step_matrix_blocked(np.zeros_like(g), g, np.zeros_like(g), hp, 32, 0)
+    g2 = g.copy()
+    g2[32:64] *= 1000.0
+    scaled = oracle.muon_step_matrix_blocked(np.zeros_like(g), g2, np.zeros_like(g), hp, 32, 0)
+    assert relf(scaled.o, base.o) <= 1e-11
+    whole = newton_schulz(g2)
+    assert relf(whole[:32], newton_schulz(g)[:32]) > 1e-2
+
+
+def test_blocked_permuting_blocks_permutes_output():
+    g = _inputs("heavy", 96, 40, 46)
+    perm = [2, 0, 1]
+    gp = np.concatenate([g[32 * k:32 * (k + 1)] for k in perm])
+    a = oracle.muon_step_matrix_blocked(np.zeros_like(g), g, np.zeros_like(g), Hyper(), 32, 0)
+    b = oracle.muon_step_matrix_blocked(np.zeros_like(g), gp, np.zeros_like(g), Hyper(), 32, 0)
+    np.testing.assert_array_equal(b.o, np.concatenate([a.o[32 * k:32 * (k + 1)] for k in perm]))
+
+
+def test_blocked_rejects_sizes_that_do_not_tile():
+    g = np.ones((10, 12))
+    for blk in [(3, 0), (0, 5), (-1, 0), (20, 0)]:
+        with pytest.raises(ValueError):
+            oracle.muon_step_matrix_blocked(g, g, g, Hyper(), *blk)
+
+
+def test_blocked_mutant_with_global_norm_fails_pin():
+    """A blocked step that normalises by the whole matrix's norm fails the per-block closed form."""
+    g = _inputs("lowrank", 128, 48, 47)
+
+    def global_norm_blocked(u, bh):
+        nu = np.linalg.norm(u)
+        out = np.empty_like(u)
+        for r0 in range(0, u.shape[0], bh):
+            x = u[r0:r0 + bh] / (nu + 1e-7)
+            tall = x.shape[0] > x.shape[1]
+            x = x.T if tall else x
+            x = oracle.ns_iterate(x, 5, A, B, C)
+            out[r0:r0 + bh] = x.T if tall else x
+        return out
+
+    assert relf(global_norm_blocked(g, 64), _blocked_closed_form(g, 64, 48)) > 1e-3
