@@ -37,6 +37,19 @@ DEFAULT_WORKLOAD = "gpt2-124m-hidden"
 GEMM_ROLES = ("ns_gram", "ns_poly", "ns_axpy", "ns_axpy_update")
 
 
+def block_of(wl, i):
+    """(block_rows, block_cols) of matrix i; (0, 0) = the whole matrix."""
+    return tuple(wl.blocks[i]) if wl.blocks is not None else (0, 0)
+
+
+def block_shapes(wl, i):
+    """Shapes of the separately orthogonalised blocks of matrix i."""
+    s = wl.mats[i]
+    br, bc = block_of(wl, i)
+    h, w = (br or s.rows), (bc or s.cols)
+    return [(h, w)] * ((s.rows // h) * (s.cols // w))
+
+
 def algorithmic_work(wl):
     """Per-launch algorithmic flops of each Newton-Schulz role and bytes of the
     momentum pass, summed over the workload's matrices.
@@ -50,11 +63,12 @@ def algorithmic_work(wl):
     ub = 2 if wl.compute == "bf16" else 4
     gram = poly = axpy = 0
     elems = 0
-    for s in wl.mats:
-        m, n = min(s.rows, s.cols), max(s.rows, s.cols)
-        gram += m * (m + 1) * n
-        poly += m * m * (m + 1)
-        axpy += 2 * m * m * n
+    for i, s in enumerate(wl.mats):
+        for (r, c) in block_shapes(wl, i):
+            m, n = min(r, c), max(r, c)
+            gram += m * (m + 1) * n
+            poly += m * m * (m + 1)
+            axpy += 2 * m * m * n
         elems += s.rows * s.cols
     return {
         "flops": {"ns_gram": gram, "ns_poly": poly, "ns_axpy": axpy, "ns_axpy_update": axpy},
@@ -154,19 +168,23 @@ def cpu_baseline(wl, grads_host, budget_s: float):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     hp = oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
-                      ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c)
+                      ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c, coeffs=wl.coeffs)
     # whole passes over the matrix list (step 1's inputs) while the budget
     # lasts; a pass that alone exceeds it stops early and is extrapolated
     done_elems, t_used, k, passes = 0, 0.0, 0, 0
     total = sum(s.rows * s.cols for s in wl.mats)
-    weights = [min(s.rows, s.cols) ** 2 * (2 * max(s.rows, s.cols) + min(s.rows, s.cols)) for s in wl.mats]
+    weights = [sum(min(r, c) ** 2 * (2 * max(r, c) + min(r, c)) for (r, c) in block_shapes(wl, i))
+               for i in range(len(wl.mats))]
     done_flops = 0
     while t_used < budget_s:
         w = oracle.decode(grads_host["param"][k])
         g = oracle.decode(grads_host["grad0"][k])
         m = np.asarray(make_momentum(wl, k), dtype=np.float64)
         t0 = time.perf_counter()
-        oracle.muon_step_matrix(w, g, m, hp)
+        if block_of(wl, k) == (0, 0):
+            oracle.muon_step_matrix(w, g, m, hp)
+        else:
+            oracle.muon_step_matrix_blocked(w, g, m, hp, *block_of(wl, k))
         t_used += time.perf_counter() - t0
         done_elems += wl.mats[k].rows * wl.mats[k].cols
         done_flops += weights[k]
@@ -252,12 +270,12 @@ def main():
     gen_s = time.perf_counter() - t_gen
 
     hp_c = nsm.Hparams(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c,
-                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute).to_c()
+                       nesterov=wl.nesterov, ns_steps=wl.ns_steps, compute=wl.compute, coeffs=wl.coeffs).to_c()
     arrays = []
     for gs in grad_sets:
         arr = (nsm.muon_matrix * n)()
         for i in range(n):
-            arr[i] = nsm.make_matrix(params[i], gs[i], moms[i])
+            arr[i] = nsm.make_matrix(params[i], gs[i], moms[i], block=block_of(wl, i))
         arrays.append(arr)
     stream = torch.cuda.current_stream(dev)
     sptr = int(stream.cuda_stream)
@@ -345,6 +363,7 @@ def main():
         "config": {
             "workload": wl.name,
             "matrices": n,
+            "plan_entries": sum(len(block_shapes(wl, i)) for i in range(n)),
             "elements": work["elements"],
             "ns_steps": wl.ns_steps,
             "storage": wl.storage,

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -77,6 +77,14 @@ typedef struct muon_matrix {
     int64_t     rows, cols;    /* stored shape, both >= 1 */
     int64_t     ld_param, ld_grad, ld_mom, ld_update;   /* leading dims, elements, >= cols */
     int32_t     dtype;         /* muon_dtype of param and grad */
+    int32_t     block_rows;    /* sub-block orthogonalisation: the matrix is cut into   */
+    int32_t     block_cols;    /* block_rows x block_cols blocks (0 = the whole dimension;
+                                  each must divide its dimension), and every block is a
+                                  matrix of its own for the norm, the transpose rule, the
+                                  iteration and the shape scale, as when query and key
+                                  weights are orthogonalised in pairs of heads ("NanoGPT
+                                  Speedrun", record list).  Momentum is elementwise and
+                                  unaffected.  0, 0 = the plain step. */
     int32_t     reserved;      /* must be 0 */
 } muon_matrix;
 
@@ -119,10 +127,13 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
  * allocates the workspace (about 8 bytes per weight element in bf16 mode, plus
  * two min(rows,cols)^2 bf16 squares per matrix); later calls with the same
  * signature allocate nothing.
+ * A matrix cut into blocks (block_rows/block_cols) enters the plan as one entry
+ * per block, in row-major block order; at most 65536 entries per call.
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
  * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
  * momentum aliasing param or grad, ns_steps outside 0..64, a == 0 or a non-finite
- * coefficient, also in coeffs, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM,
+ * coefficient, also in coeffs, a block size < 0 or not dividing its dimension,
+ * more than 65536 entries, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM,
  * MUON_ERR_HIP. */
 muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
                       const muon_hparams *hp, void *stream);
@@ -137,7 +148,8 @@ muon_status muon_orthogonalize(muon_handle *h, const void *in, float *out,
                                int32_t in_dtype, const muon_hparams *hp, void *stream);
 
 /* Frobenius norms ||u||_F of the orthogonalised inputs of the most recent
- * muon_step, in list order, copied to host memory `out` (n entries; the call
+ * muon_step, one per plan entry (a blocked matrix has one per block, row-major)
+ * in list order, copied to host memory `out` (n entries; the call
  * synchronises the stream).  Validation hook. */
 muon_status muon_read_norms(muon_handle *h, float *out, int32_t n, void *stream);
 

@@ -191,6 +191,7 @@ class Workload:
     b: float = -4.7750
     c: float = 2.0315
     coeffs: Optional[Tuple[Tuple[float, float, float], ...]] = None   # per-iteration triples, None = (a, b, c)
+    blocks: Optional[Tuple[Tuple[int, int], ...]] = None   # per-matrix (block_rows, block_cols), 0 = whole
     expert_scale_range: Tuple[float, float] = (-4.0, -1.0)
     description: str = ""
 
@@ -210,6 +211,11 @@ def _gpt2_set(layers: int, d: int, ff: int) -> Tuple[MatSpec, ...]:
         out.append(MatSpec(d, ff, f"h{l}.mlp.up"))
         out.append(MatSpec(ff, d, f"h{l}.mlp.down"))
     return tuple(out)
+
+
+def _qk_pairs(mats: Tuple[MatSpec, ...], rows: int) -> Tuple[Tuple[int, int], ...]:
+    """Block sizes: query and key weights cut into `rows`-row blocks, the rest whole."""
+    return tuple((rows, 0) if m.name.endswith((".q", ".k")) else (0, 0) for m in mats)
 
 
 def _large_share() -> Tuple[MatSpec, ...]:
@@ -239,6 +245,10 @@ WORKLOADS: Dict[str, Workload] = {
                  description="one 64x128 float32 matrix, W/G/M ~ N(0, 0.02^2), one step, fp32 mode"),
         Workload("gpt2-124m-hidden", 2, _gpt2_set(12, 768, 3072), steps=10,
                  description="GPT-2 124M hidden matrices: 12 x {4 x 768x768, 768x3072, 3072x768}"),
+        Workload("gpt2-124m-hidden-qk-head-pairs", 6, _gpt2_set(12, 768, 3072), steps=10,
+                 blocks=_qk_pairs(_gpt2_set(12, 768, 3072), 2 * 64),
+                 description="the GPT-2 124M set with every query and key weight orthogonalised in "
+                             "pairs of 64-wide heads (6 blocks of 128x768 each)"),
         Workload("gpt2-350m-hidden", 3, _gpt2_set(24, 1024, 4096), steps=10, nesterov=True,
                  weight_decay=0.01,
                  description="GPT-2 350M-style: 24 x {4 x 1024x1024, 1024x4096, 4096x1024}, Nesterov, wd 0.01"),

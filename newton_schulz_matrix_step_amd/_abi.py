@@ -14,6 +14,7 @@ from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_mi355x.so")
+ABI_VERSION = 3   # the MUON_ABI_VERSION of the header this binding mirrors
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1
@@ -58,6 +59,8 @@ class muon_matrix(ctypes.Structure):
         ("ld_mom", ctypes.c_int64),
         ("ld_update", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
+        ("block_rows", ctypes.c_int32),
+        ("block_cols", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -103,6 +106,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.muon_abi_version.restype = ctypes.c_int
     lib.muon_abi_version.argtypes = []
+    if lib.muon_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} implements ABI version {lib.muon_abi_version()}, the binding expects "
+                          f"{ABI_VERSION}: rebuild the library")
     lib.muon_init.restype = ctypes.c_int
     lib.muon_init.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_uint32]
     lib.muon_step.restype = ctypes.c_int
@@ -198,25 +204,31 @@ def muon_init(device: int = 0, flags: int = 0) -> int:
     return h.value
 
 
-def make_matrix(param, grad, momentum, update_out=None) -> muon_matrix:
-    """Describe one weight's tensors (device tensors, unit column stride)."""
+def make_matrix(param, grad, momentum, update_out=None, block=(0, 0)) -> muon_matrix:
+    """Describe one weight's tensors (device tensors, unit column stride);
+    ``block`` = (block_rows, block_cols) cuts it into separately orthogonalised
+    blocks (0 = the whole dimension)."""
     return muon_matrix(
         param.data_ptr(), grad.data_ptr(), momentum.data_ptr(),
         update_out.data_ptr() if update_out is not None else None,
         int(param.shape[0]), int(param.shape[1]),
         _ld(param), _ld(grad), _ld(momentum), _ld(update_out) if update_out is not None else 0,
-        _dtype_code(param) if _dtype_code(param) == _dtype_code(grad) else -1, 0)
+        _dtype_code(param) if _dtype_code(param) == _dtype_code(grad) else -1,
+        int(block[0]), int(block[1]), 0)
 
 
 def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp: Hparams,
-              update_outs: Optional[Sequence] = None, stream=None) -> None:
-    """One Muon step over every (param, grad, momentum) triple, on ``stream``."""
+              update_outs: Optional[Sequence] = None, stream=None, blocks: Optional[Sequence] = None) -> None:
+    """One Muon step over every (param, grad, momentum) triple, on ``stream``;
+    ``blocks[i]`` = (block_rows, block_cols) of matrix i, or None for all (0, 0)."""
     n = len(params)
-    if len(grads) != n or len(moms) != n or (update_outs is not None and len(update_outs) != n):
-        raise ValueError("params, grads, moms (and update_outs) must have the same length")
+    if len(grads) != n or len(moms) != n or (update_outs is not None and len(update_outs) != n) or \
+            (blocks is not None and len(blocks) != n):
+        raise ValueError("params, grads, moms (and update_outs, blocks) must have the same length")
     arr = (muon_matrix * max(n, 1))()
     for i in range(n):
-        arr[i] = make_matrix(params[i], grads[i], moms[i], update_outs[i] if update_outs is not None else None)
+        arr[i] = make_matrix(params[i], grads[i], moms[i], update_outs[i] if update_outs is not None else None,
+                             blocks[i] if blocks is not None else (0, 0))
     c_hp = hp.to_c()
     st = load().muon_step(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream))
     _check(handle, st)

@@ -40,6 +40,7 @@ constexpr int kStageSlots = 4;
 constexpr int kMaxNsSteps = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxEntries = 65536;   // plan entries (matrices or blocks) per muon_step call
 constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
 
 
@@ -195,6 +196,37 @@ muon_status validate_mat(muon_handle* h, const MatIn& m, int idx) {
     if (m.upd && (static_cast<const void*>(m.upd) == g || static_cast<void*>(m.upd) == m.param ||
                   (m.has_mom && m.upd == m.mom)))
         return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: update_out aliases another buffer", idx);
+    return MUON_OK;
+}
+
+// Sub-block orthogonalisation: a validated matrix cut into bh x bw blocks
+// enters the plan as one entry per block (row-major), each a strided view of
+// the caller's buffers with the whole matrix's leading dimensions.
+muon_status append_blocks(muon_handle* h, const MatIn& m, int32_t block_rows, int32_t block_cols, int idx,
+                          std::vector<MatIn>& out) {
+    if (block_rows < 0 || block_cols < 0)
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: negative block size %d x %d", idx, block_rows, block_cols);
+    const int64_t bh = block_rows ? block_rows : m.R;
+    const int64_t bw = block_cols ? block_cols : m.C;
+    if (m.R % bh != 0 || m.C % bw != 0)
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: block %lld x %lld does not tile %lld x %lld", idx,
+                    (long long)bh, (long long)bw, (long long)m.R, (long long)m.C);
+    const int64_t nb = (m.R / bh) * (m.C / bw);
+    if (int64_t(out.size()) + nb > kMaxEntries)
+        return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: more than %lld plan entries in one call", idx,
+                    (long long)kMaxEntries);
+    const int64_t es = m.dtype == MUON_BF16 ? 2 : 4;
+    for (int64_t r0 = 0; r0 < m.R; r0 += bh)
+        for (int64_t c0 = 0; c0 < m.C; c0 += bw) {
+            MatIn b = m;
+            b.R = bh;
+            b.C = bw;
+            b.grad = static_cast<const char*>(m.grad) + (r0 * m.ld_grad + c0) * es;
+            if (m.param) b.param = static_cast<char*>(m.param) + (r0 * m.ld_param + c0) * es;
+            if (m.mom) b.mom = m.mom + (r0 * m.ld_mom + c0);
+            if (m.upd) b.upd = m.upd + (r0 * m.ld_upd + c0);
+            out.push_back(b);
+        }
     return MUON_OK;
 }
 
@@ -563,13 +595,16 @@ muon_status muon_step(muon_handle* h, const muon_matrix* mats, int32_t n_mats, c
     if (!mats) return fail(h, MUON_ERR_INVALID_ARG, "mats is NULL");
     muon_status st = validate_hp(h, hp);
     if (st != MUON_OK) return st;
-    std::vector<MatIn> in(n_mats);
+    std::vector<MatIn> in;
+    in.reserve(size_t(n_mats));
     for (int i = 0; i < n_mats; ++i) {
         const muon_matrix& m = mats[i];
         if (m.reserved != 0) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: reserved field must be 0", i);
-        in[i] = MatIn{m.param, m.grad, m.momentum, m.update_out, m.rows, m.cols, m.ld_param,
-                      m.ld_grad, m.ld_mom, m.update_out ? m.ld_update : 0, m.dtype, true, true};
-        st = validate_mat(h, in[i], i);
+        const MatIn whole{m.param, m.grad, m.momentum, m.update_out, m.rows, m.cols, m.ld_param,
+                          m.ld_grad, m.ld_mom, m.update_out ? m.ld_update : 0, m.dtype, true, true};
+        st = validate_mat(h, whole, i);
+        if (st != MUON_OK) return st;
+        st = append_blocks(h, whole, m.block_rows, m.block_cols, i, in);
         if (st != MUON_OK) return st;
     }
     DeviceGuard g(h->device);

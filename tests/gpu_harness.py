@@ -85,6 +85,13 @@ def oracle_hyper(wl: Workload) -> oracle.Hyper:
                         coeffs=wl.coeffs)
 
 
+def shape_scales(shape, block=(0, 0)) -> np.ndarray:
+    """Elementwise shape scale sqrt(max(1, h/w)) of the block each element belongs to."""
+    bh = shape[0] if block[0] == 0 else block[0]
+    bw = shape[1] if block[1] == 0 else block[1]
+    return np.full(shape, math.sqrt(max(1.0, bh / bw)))
+
+
 @dataclass
 class StepRecord:
     w_old: np.ndarray    # stored representation before the step
@@ -113,7 +120,7 @@ def run_gpu(wl: Workload, steps: int, check: Sequence[int], handle=None, grad_fn
             g_stored = [encode_storage(gf(wl, s, i), wl.storage) for i in range(n)]
             grads = [to_device(x) for x in g_stored]
             w_old = {i: to_stored(params[i]) for i in check}
-            nsm.muon_step(h, params, grads, moms, hp, update_outs=upd)
+            nsm.muon_step(h, params, grads, moms, hp, update_outs=upd, blocks=wl.blocks)
             torch.cuda.synchronize()
             for i in check:
                 rec[i].append(StepRecord(w_old[i], to_stored(params[i]), to_stored(moms[i]), to_stored(upd[i]),
@@ -134,7 +141,11 @@ def check_against_oracle(wl: Workload, rec: Dict[int, List[StepRecord]], tol_o: 
         for s, r in enumerate(steps):
             w_old = oracle.decode(r.w_old)
             g = oracle.decode(r.g)
-            res = oracle.muon_step_matrix(w_old, g, m, hp)
+            blk = wl.blocks[i] if wl.blocks is not None else (0, 0)
+            if blk == (0, 0):
+                res = oracle.muon_step_matrix(w_old, g, m, hp)
+            else:
+                res = oracle.muon_step_matrix_blocked(w_old, g, m, hp, *blk)
             e_m = relf(r.m_new, res.m)
             e_o = relf(r.o, res.o)
             if report is not None:
@@ -143,7 +154,7 @@ def check_against_oracle(wl: Workload, rec: Dict[int, List[StepRecord]], tol_o: 
             assert e_m <= TOL_MOM, f"matrix {i} step {s + 1}: momentum rel err {e_m:.3e}"
             assert e_o <= tol_o, f"matrix {i} step {s + 1}: O rel err {e_o:.3e} > {tol_o}"
             # the stored weight: float64 update of the GPU's own O, rounded once
-            sc = math.sqrt(max(1.0, r.w_old.shape[0] / r.w_old.shape[1]))
+            sc = shape_scales(r.w_old.shape, blk)
             w_exp = w_old * (1.0 - wl.lr * wl.weight_decay) - wl.lr * sc * r.o.astype(np.float64)
             if r.w_new.dtype == np.uint16:
                 ok = weight_error_ok(r.w_new, w_old, r.o.astype(np.float64), wl.lr, wl.weight_decay, sc)

@@ -47,16 +47,18 @@ def test_struct_layout_matches_header(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "muon.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(muon_matrix), sizeof(muon_hparams),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(muon_matrix), sizeof(muon_hparams),"
         " sizeof(muon_kernel_stats), offsetof(muon_matrix, dtype), offsetof(muon_hparams, ns_steps),"
-        " offsetof(muon_matrix, ld_update), offsetof(muon_hparams, coeffs)); return 0;}\n")
+        " offsetof(muon_matrix, ld_update), offsetof(muon_hparams, coeffs), offsetof(muon_matrix, block_rows),"
+        " offsetof(muon_matrix, block_cols)); return 0;}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
     out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert out == [ctypes.sizeof(_abi.muon_matrix), ctypes.sizeof(_abi.muon_hparams),
                    ctypes.sizeof(_abi.muon_kernel_stats), _abi.muon_matrix.dtype.offset,
                    _abi.muon_hparams.ns_steps.offset, _abi.muon_matrix.ld_update.offset,
-                   _abi.muon_hparams.coeffs.offset]
+                   _abi.muon_hparams.coeffs.offset, _abi.muon_matrix.block_rows.offset,
+                   _abi.muon_matrix.block_cols.offset]
 
 
 def test_status_strings(lib):

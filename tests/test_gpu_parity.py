@@ -212,3 +212,59 @@ def test_invalid_schedule_rejected(bad):
         assert float(w.abs().max()) == 0.0 and float(m.abs().max()) == 0.0   # nothing ran
     finally:
         nsm.muon_destroy(h)
+
+
+# sub-block orthogonalisation: query/key style weights cut into pairs of heads
+BLOCK_SHAPES = [(768, 768), (2304, 768), (192, 160), (130, 60), (300, 100)]
+BLOCKS = ((128, 0), (128, 0), (64, 80), (65, 0), (0, 0))
+
+
+@pytest.mark.parametrize("compute,tol", [("bf16", TOL_O_BF16), ("fp32", 1e-4)])
+def test_blocked_orthogonalisation(compute, tol):
+    wl = _wl("blocked", BLOCK_SHAPES, steps=2, nesterov=True, weight_decay=0.01, compute=compute, blocks=BLOCKS)
+    rep = []
+    rec = run_gpu(wl, 2, list(range(len(BLOCK_SHAPES))))
+    check_against_oracle(wl, rec, tol, tol_w_f32=tol, report=rep)
+    print(compute, "blocked worst O rel err", max(e for (_, _, _, e) in rep))
+
+
+def test_blocked_norms_and_whole_block_bitwise():
+    """Norm readback has one entry per block; a block covering the whole matrix
+    is the plain step, bit for bit."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    wl = _wl("wholeblk", [(300, 100), (128, 384)], steps=1)
+    a = run_gpu(wl, 1, [0, 1])
+    b = run_gpu(wl.with_(blocks=((300, 100), (128, 384))), 1, [0, 1])
+    for i in (0, 1):
+        assert np.array_equal(a[i][0].o, b[i][0].o) and np.array_equal(a[i][0].w_new, b[i][0].w_new)
+    h = nsm.muon_init(0)
+    try:
+        g = torch.randn(256, 96, device="cuda")
+        w, m = torch.zeros_like(g), torch.zeros_like(g)
+        nsm.muon_step(h, [w, torch.zeros(8, 8, device="cuda")], [g, torch.ones(8, 8, device="cuda")],
+                      [m, torch.zeros(8, 8, device="cuda")], nsm.Hparams(compute="fp32"), blocks=[(64, 48), (0, 0)])
+        nu = nsm.muon_read_norms(h, 9)
+        gd = g.double().cpu()
+        expect = [float(torch.linalg.norm(gd[r:r + 64, c:c + 48])) for r in range(0, 256, 64) for c in (0, 48)]
+        assert nu[:8] == pytest.approx(expect, rel=1e-6)
+        assert nu[8] == pytest.approx(8.0, rel=1e-6)
+    finally:
+        nsm.muon_destroy(h)
+
+
+@pytest.mark.parametrize("block", [(3, 0), (0, 5), (-1, 0), (20, 0), (1, 1)])
+def test_invalid_block_rejected(block):
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    shape = (300, 300) if block == (1, 1) else (10, 12)     # (1, 1) blocks: 90000 entries, over the limit
+    h = nsm.muon_init(0)
+    try:
+        g = torch.randn(*shape, device="cuda")
+        w, m = torch.zeros_like(g), torch.zeros_like(g)
+        with pytest.raises(nsm.MuonError) as ei:
+            nsm.muon_step(h, [w], [g], [m], nsm.Hparams(), blocks=[block])
+        assert ei.value.status == nsm.MUON_ERR_INVALID_ARG
+        assert float(w.abs().max()) == 0.0 and float(m.abs().max()) == 0.0
+    finally:
+        nsm.muon_destroy(h)
