@@ -124,7 +124,7 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
 
 /* One Muon step over `n_mats` matrices (all steps above), enqueued on `stream`.
  * The first call for a given list of shapes/dtypes/compute mode builds a plan and
- * allocates the workspace (about 8 bytes per weight element in bf16 mode, plus
+ * allocates the workspace (about 7 bytes per weight element in bf16 mode, plus
  * two min(rows,cols)^2 bf16 squares per matrix); later calls with the same
  * signature allocate nothing.
  * A matrix cut into blocks (block_rows/block_cols) enters the plan as one entry

@@ -270,7 +270,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         d.shape_scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));
         const int64_t xe = int64_t(d.mp) * d.np;
         d.off_u = take(int64_t(d.Rp) * d.Cp * es);
-        d.off_xlo = f32c ? 0 : take(xe * 2);
+        d.off_xlo = f32c ? 0 : take(xe);
         d.off_xb0 = take(xe * es);
         d.off_xb1 = take(xe * es);
         d.off_a = take(int64_t(d.mp) * d.mp * es);

@@ -30,7 +30,7 @@ struct MatDesc {
     float shape_scale;         // sqrt(max(1, R / C))
     int32_t pad0;
     int64_t off_u;             // workspace byte offsets
-    int64_t off_xlo;           // bf16 mode: X - bf16(X) in bf16; with the operand copy, the master X
+    int64_t off_xlo;           // bf16 mode: X - bf16(X) in one byte per element; with the operand copy, the master X
     int64_t off_xb0, off_xb1;  // operand copies of X, ping-pong
     int64_t off_a, off_b;      // A = X X^T and B = b A + c A^2 (mp x mp)
     void* param;

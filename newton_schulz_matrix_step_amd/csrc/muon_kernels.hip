@@ -52,6 +52,24 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Low part of the master X in one byte: the remainder x - bf16(x) counted in
+// units of 1/256 of the bf16 spacing at hi (spacing 2^(E-134) for biased
+// exponent E >= 1, the denormal spacing for E = 0), rounded to nearest and
+// stored offset by 128.  The remainder of a round-to-nearest is at most half
+// a spacing, 128 units; hi + lo then holds x to 2^-16 relative.
+__device__ __forceinline__ int lo8_unit_exp(uint32_t hbits) {
+    const int e = int((hbits >> 7) & 0xFFu);
+    return (e < 1 ? 1 : e) - 142;
+}
+__device__ __forceinline__ uint32_t enc_lo8(float rem, uint32_t hbits) {
+    float q = __builtin_rintf(ldexpf(rem, -lo8_unit_exp(hbits)));
+    q = fminf(fmaxf(q, -127.f), 127.f);
+    return uint32_t(int(q) + 128);
+}
+__device__ __forceinline__ float dec_lo8(uint32_t byte, uint32_t hbits) {
+    return ldexpf(float(byte) - 128.f, lo8_unit_exp(hbits));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
@@ -903,7 +921,7 @@ __device__ __forceinline__ IoView io_view(const MatDesc& md, bool nest) {
 // optional fp32 copy of O.  Runs are 4 consecutive stored columns of one row.
 struct AxpyCtx {
     const uint16_t* xhi;       // current X, bf16 (the operand copy this GEMM reads)
-    uint16_t* xlo;             // X - hi, bf16: with hi, the master copy of X
+    uint8_t* xlo;              // X - hi in 8 bits (enc_lo8): with hi, the master copy of X
     uint16_t* xb_next;
     int64_t ldq;
     int R, C;
@@ -1002,8 +1020,8 @@ __device__ __forceinline__ void axpy_load(const AxpyCtx& x, const HiCap<TI>& cap
             u32x2_t hi;
             if constexpr (CAPHI) hi = cap.v[band][q];
             else hi = *gm(reinterpret_cast<const u32x2_t*>(x.xhi + off));
-            const u32x2_t lo = *gm(reinterpret_cast<const u32x2_t*>(x.xlo + off));
-            w.ra[q] = u32x4_t{hi[0], hi[1], lo[0], lo[1]};
+            const uint32_t lo = *gm(reinterpret_cast<const uint32_t*>(x.xlo + off));
+            w.ra[q] = u32x4_t{hi[0], hi[1], lo, 0u};
         } else {
             w.ra[q] = u32x4_t{0u, 0u, 0u, 0u};
             w.rb[q] = u32x4_t{0u, 0u, 0u, 0u};
@@ -1039,7 +1057,10 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         nv = nv > 4 ? 4 : nv;
         f32x4_t mst;
         if (!FIRST) {
-            mst = dec4(w.ra[q], 0) + dec4(u32x4_t{w.ra[q][2], w.ra[q][3], 0u, 0u}, 0);
+            mst = dec4(w.ra[q], 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mst[k] += dec_lo8((w.ra[q][2] >> (8 * k)) & 0xFFu, w.ra[q][k >> 1] >> (16 * (k & 1)));
         } else if (io_mom<M>(x.io)) {
             mst = dec4(w.ra[q], 1);
             if (io_nest<M>(x.io)) {
@@ -1053,26 +1074,26 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
         const f32x4_t o = x.alpha * (x.a * (mst + v));   // acc holds (B / a) X
         if (!LAST) {
-            // X' = hi + lo: hi its bf16 rounding, lo the bf16 rounding of the
+            // X' = hi + lo: hi its bf16 rounding, lo the 8-bit code of the
             // (exact) remainder
             const int64_t off = int64_t(r) * x.ldq + c;
-            uint16_t h[4], l[4];
+            uint16_t h[4];
+            uint32_t l = 0u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
                 h[q2] = f32_to_bf16(o[q2]);
-                l[q2] = f32_to_bf16(o[q2] - bf16_to_f32(h[q2]));
+                l |= enc_lo8(o[q2] - bf16_to_f32(h[q2]), h[q2]) << (8 * q2);
             }
             if (!EDGE || nv == 4) {
                 *gm(reinterpret_cast<u32x2_t*>(x.xb_next + off)) =
                     u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-                *gm(reinterpret_cast<u32x2_t*>(x.xlo + off)) =
-                    u32x2_t{uint32_t(l[0]) | (uint32_t(l[1]) << 16), uint32_t(l[2]) | (uint32_t(l[3]) << 16)};
+                *gm(reinterpret_cast<uint32_t*>(x.xlo + off)) = l;
             } else {
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
                     if (q2 < nv) {
                         gm(x.xb_next)[off + q2] = h[q2];
-                        gm(x.xlo)[off + q2] = l[q2];
+                        gm(x.xlo)[off + q2] = uint8_t(l >> (8 * q2));
                     }
             }
         } else {
@@ -1089,12 +1110,22 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
     }
 }
 
-template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI, bool PRE>
-__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>& cap, const AxpyRaw<TI>& w0,
+// PRE bands' raw operands arrive in wp (loaded during the last k block); with
+// PRE = TI the epilogue issues no load at all.
+template <int TI, bool FIRST, bool LAST, bool EDGE, class M, bool CAPHI, int PRE>
+__device__ __forceinline__ void epi_axpy_body(const AxpyCtx& x, const HiCap<TI>& cap, const AxpyRaw<TI> (&wp)[PRE ? PRE : 1],
                                               const f32x4_t (&acc)[TI][TI], int row0, int col0, int lane,
                                               float* __restrict__ stg) {
+    if constexpr (PRE == TI) {
+        static_for<0, TI>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            stage_band<TI>(stg, acc, i, lane);
+            axpy_store<TI, FIRST, LAST, EDGE, M>(x, stg, row0, col0, lane, i, wp[i]);
+        });
+        return;
+    }
     AxpyRaw<TI> w[2];
-    if constexpr (PRE) w[0] = w0;
+    if constexpr (PRE > 0) w[0] = wp[0];
     else axpy_load<TI, FIRST, LAST, EDGE, M, CAPHI>(x, cap, row0, col0, lane, 0, w[0]);
     static_for<0, TI>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
@@ -1110,7 +1141,7 @@ __device__ __forceinline__ AxpyCtx axpy_ctx(const MatDesc& md, const Tile& t, co
     AxpyCtx x;
     const int it = pa.iter;
     x.xhi = reinterpret_cast<const uint16_t*>(pa.ws + (((it - 2) & 1) ? md.off_xb1 : md.off_xb0));   // it >= 2
-    x.xlo = reinterpret_cast<uint16_t*>(pa.ws + md.off_xlo);
+    x.xlo = reinterpret_cast<uint8_t*>(pa.ws + md.off_xlo);
     x.xb_next = reinterpret_cast<uint16_t*>(pa.ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0));
     x.ldq = md.Cp;
     x.R = md.R;
@@ -1125,10 +1156,10 @@ __device__ __forceinline__ AxpyCtx axpy_ctx(const MatDesc& md, const Tile& t, co
     return x;
 }
 
-// PRE: band 0's raw operands were loaded during the last k block (w0).
-template <int TI, bool FIRST, bool LAST, bool CAPHI, bool PRE>
+// PRE: the first PRE bands' raw operands were loaded during the last k block (w0).
+template <int TI, bool FIRST, bool LAST, bool CAPHI, int PRE>
 __device__ __forceinline__ void epi_axpy(const AxpyCtx& x, const f32x4_t (&acc)[TI][TI], const HiCap<TI>& cap,
-                                         const AxpyRaw<TI>& w0, int row0, int col0, int lane,
+                                         const AxpyRaw<TI> (&w0)[PRE ? PRE : 1], int row0, int col0, int lane,
                                          float* __restrict__ stg) {
     constexpr int WT = EpiGeom<TI>::WT;
     if (!(x.vio && row0 + WT <= x.R && col0 + WT <= x.C)) {
@@ -1328,21 +1359,26 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restri
     if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
         constexpr bool LAST = KIND == PH_AXPY_LAST;
         // 128-wide tiles after the first iteration keep the bf16 X of their own
-        // quadrant from the operand stream (see HiCap), and all but the last
-        // iteration issue the epilogue's first band of loads during the last
-        // k block
+        // quadrant from the operand stream (see HiCap).  The first iteration
+        // issues the epilogue's first band of loads during the last k block;
+        // the middle ones, which load only the low part of the master, issue
+        // every band's loads there (4 words a lane), so the epilogue never
+        // waits on memory band by band.
         constexpr bool CAPHI = !FIRST && BM == 128 && WT == kBK;
-        constexpr bool PRE = BM == 128 && !LAST;   // (measured slower on the last iteration)
+        constexpr int PRE = BM != 128 || LAST ? 0 : (CAPHI ? TI : 1);   // (measured slower on the last iteration)
         const AxpyCtx x = axpy_ctx<FIRST>(md, t, pa);
-        AxpyRaw<TI> w0;
+        AxpyRaw<TI> w0[PRE ? PRE : 1];
         const int er0 = row_a0 + wr, ec0 = row_b0 + wc;
         auto pre = [&]() __attribute__((always_inline)) {
-            axpy_load<TI, FIRST, LAST, true, IoRuntime, CAPHI>(x, cap, er0, ec0, lane, 0, w0);
+            static_for<0, PRE>([&](auto bc) {
+                axpy_load<TI, FIRST, LAST, true, IoRuntime, CAPHI>(x, cap, er0, ec0, lane, decltype(bc)::value,
+                                                                   w0[decltype(bc)::value]);
+            });
         };
         auto run = [&](auto capc, auto akc) __attribute__((always_inline)) {
             constexpr int CAPV = decltype(capc)::value;
             constexpr bool AKC_ALL = decltype(akc)::value;
-            if constexpr (PRE)
+            if constexpr (PRE > 0)
                 mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap, pre);
             else
                 mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
