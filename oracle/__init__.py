@@ -29,3 +29,4 @@ from .muon_oracle import (  # noqa: F401
     shape_scale,
     update_direction,
 )
+from .adamw_oracle import AdamWHyper, AdamWResult, adamw_step  # noqa: F401,E402
