@@ -10,6 +10,9 @@ the timed region starts.
 Prints ONE JSON line (rank 0): steps/s as ``value``, plus the Newton-Schulz
 TFLOP/s, a roofline entry for the dominant kernel (HIP-event timed launches)
 and the CPU float64 oracle timed on a bounded sample of the same workload.
+
+``--workload gpt2-124m-adamw-params`` measures the AdamW step of the hybrid
+setup's other parameters instead (``muon_adamw_step``), against HBM.
 """
 
 from __future__ import annotations
@@ -79,6 +82,7 @@ def algorithmic_work(wl):
 
 
 KERNEL_SOURCES = ("newton_schulz_matrix_step_amd/csrc/muon_kernels.hip",
+                  "newton_schulz_matrix_step_amd/csrc/adamw_kernels.hip",
                   "newton_schulz_matrix_step_amd/csrc/muon_api.cpp",
                   "newton_schulz_matrix_step_amd/csrc/muon_internal.hpp")
 
@@ -210,6 +214,126 @@ def cpu_baseline(wl, grads_host, budget_s: float):
     }
 
 
+def adamw_bench(args):
+    """AdamW over the workload's tensors: one grouped launch a step, inputs
+    resident in HBM; bytes per element: read p, g, m, v and write p, m, v."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    from muon_synth import adamw_workload, encode_storage, make_adamw_grad, make_adamw_param
+
+    wl = adamw_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = len(wl.tensors)
+    n_sets = args.grad_sets or 2
+
+    def upload(stored):
+        if stored.dtype == np.uint16:
+            return torch.from_numpy(stored.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(stored, dtype=np.float32)).to(dev)
+
+    t_gen = time.perf_counter()
+    host_p = [encode_storage(make_adamw_param(wl, i), wl.storage) for i in range(n)]
+    params = [upload(x) for x in host_p]
+    ms = [torch.zeros(t.numel, device=dev) for t in wl.tensors]
+    vs = [torch.zeros(t.numel, device=dev) for t in wl.tensors]
+    host_g0 = None
+    grad_sets = []
+    for s in range(1, n_sets + 1):
+        st = [encode_storage(make_adamw_grad(wl, s, i), wl.storage) for i in range(n)]
+        if s == 1:
+            host_g0 = st
+        grad_sets.append([upload(x) for x in st])
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t_gen
+
+    arrays = []
+    for gs in grad_sets:
+        arr = (nsm.muon_adamw_tensor * n)()
+        for i in range(n):
+            arr[i] = nsm.make_adamw_tensor(params[i], gs[i], ms[i], vs[i])
+        arrays.append(arr)
+    sptr = int(torch.cuda.current_stream(dev).cuda_stream)
+    step_no = [0]
+
+    def run_steps(h, k):
+        for _ in range(k):
+            step_no[0] += 1
+            hp = nsm.AdamWHparams(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                                  weight_decay=wl.weight_decay, step=step_no[0]).to_c()
+            st = nsm.muon_adamw_step_raw(h, arrays[step_no[0] % n_sets], n, hp, sptr)
+            if st != 0:
+                raise nsm.MuonError(st, nsm.muon_last_error(h))
+
+    h = nsm.muon_init(0, nsm.MUON_INIT_PROFILE)
+    run_steps(h, args.warmup)
+    torch.cuda.synchronize()
+    nsm.muon_kernel_stats_reset(h)
+    t0 = time.perf_counter()
+    run_steps(h, args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = nsm.muon_kernel_stats_read(h)
+    nsm.muon_destroy(h)
+    ms_per_step = elapsed * 1e3 / args.steps
+    launches, total_ms = stats["adamw"]
+    avg_s = total_ms * 1e-3 / launches
+    eb = (2 + 2 + 4 + 4 + 2 + 4 + 4) if wl.storage == "bf16" else (4 + 4 + 4 + 4 + 4 + 4 + 4)
+    bytes_per_launch = wl.elements * eb
+    achieved = bytes_per_launch / avg_s / 1e9
+    out = {
+        "metric": "AdamW steps/sec, GPT-2-124M non-matrix parameter set, 1 GPU",
+        "value": round(1e3 / ms_per_step, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tensors": n, "elements": wl.elements, "storage": wl.storage,
+                   "grad_sets": n_sets},
+        "roofline": {"kernel": "adamw_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": bytes_per_launch, "bytes_per_element": eb},
+        "kernels": {"adamw": {"launches": launches, "avg_us": round(avg_s * 1e6, 2)}},
+        "input_gen_s": round(gen_s, 1),
+    }
+    tr = recorded_traffic("adamw", wl.name)
+    if tr is not None:
+        out["roofline"]["traffic"] = round(tr["fetch"] + tr["write"])
+        out["roofline"]["traffic_fetch"] = round(tr["fetch"])
+        out["roofline"]["traffic_write"] = round(tr["write"])
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
+                        default=1)
+        except Exception:  # pragma: no cover
+            cores = 1
+        hyper = oracle.AdamWHyper(lr=wl.lr, beta1=wl.beta1, beta2=wl.beta2, eps=wl.eps,
+                                  weight_decay=wl.weight_decay)
+        done, t_used, k = 0, 0.0, 0
+        while t_used < args.cpu_budget and k < n:
+            p = oracle.decode(host_p[k])
+            g = oracle.decode(host_g0[k])
+            z = np.zeros_like(p)
+            t1 = time.perf_counter()
+            oracle.adamw_step(p, g, z, z, hyper, 1)
+            t_used += time.perf_counter() - t1
+            done += wl.tensors[k].numel
+            k += 1
+        out["cpu_baseline"] = {"value": round(1.0 / (t_used * wl.elements / max(done, 1)), 4), "unit": "steps/s",
+                               "cores": int(cores), "kind": "oracle",
+                               "sample": f"{k} of {n} tensors of step 1 ({done}/{wl.elements} elements), "
+                                         f"{t_used:.1f} s of float64 NumPy, extrapolated by elements"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,13 +356,17 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported by this build "
-              "(every matrix's step is independent; the multi-GPU sharding is a design note, not code)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (every matrix's step is "
+              "independent and the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+
+    from muon_synth import ADAMW_WORKLOADS
+    if args.workload in ADAMW_WORKLOADS:
+        adamw_bench(args)
         return
 
     import torch

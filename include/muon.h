@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -114,6 +114,28 @@ typedef struct muon_kernel_stats {
     double  total_ms;          /* summed HIP-event durations */
 } muon_kernel_stats;
 
+/* One tensor of the list handed to muon_adamw_step: any parameter Muon does not
+ * take (embeddings, output head, norm gains, biases), as `numel` contiguous
+ * elements. */
+typedef struct muon_adamw_tensor {
+    void       *param;         /* numel elements, `dtype`, updated in place */
+    const void *grad;          /* numel elements, `dtype`, read only */
+    float      *exp_avg;       /* numel float32, first moment, updated in place (start at 0) */
+    float      *exp_avg_sq;    /* numel float32, second moment, updated in place (start at 0) */
+    int64_t     numel;         /* >= 0; 0 = nothing to do for this entry */
+    int32_t     dtype;         /* muon_dtype of param and grad */
+    int32_t     reserved;      /* must be 0 */
+} muon_adamw_tensor;
+
+/* AdamW hyperparameters, shared by every tensor of one call. */
+typedef struct muon_adamw_hparams {
+    float   lr;                /* learning rate, finite */
+    float   beta1, beta2;      /* moment decays, each in [0, 1) */
+    float   eps;               /* added to sqrt of the corrected second moment, finite, > 0 */
+    float   weight_decay;      /* decoupled: p *= 1 - lr * weight_decay, finite */
+    int32_t step;              /* 1-based step count t of this update (bias corrections 1 - beta^t) */
+} muon_adamw_hparams;
+
 /* Version of this header the library was built from (MUON_ABI_VERSION). */
 int muon_abi_version(void);
 
@@ -146,6 +168,26 @@ muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
 muon_status muon_orthogonalize(muon_handle *h, const void *in, float *out,
                                int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
                                int32_t in_dtype, const muon_hparams *hp, void *stream);
+
+/* One AdamW step over `n` tensors, enqueued on `stream`: for every element
+ *
+ *   m' = beta1 m + (1 - beta1) g ;  v' = beta2 v + (1 - beta2) g^2
+ *   p' = p (1 - lr wd) - lr (m' / (1 - beta1^t)) / (sqrt(v' / (1 - beta2^t)) + eps)
+ *
+ * in float32 arithmetic (param rounded once to its dtype).  This is the update
+ * the hybrid setup runs on the parameters Muon does not take ("14 --
+ * modded-nanogpt", section 3; the Muon page, "Where Muon does not apply"); the
+ * pages give no formula, so it is the standard AdamW (Loshchilov and Hutter,
+ * decoupled weight decay, bias-corrected Adam moments).  One launch covers the
+ * whole list.  The first call for a list of sizes/dtypes builds a plan (a few
+ * bytes of device tables per 4096 elements); later calls with the same sizes
+ * allocate nothing.  n == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null
+ * handle/tensors/hp with n > 0, a null buffer with numel > 0, numel < 0,
+ * buffers of one tensor aliasing each other, beta outside [0, 1), eps <= 0,
+ * a non-finite lr/eps/weight_decay, step < 1, reserved != 0, n < 0),
+ * MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
+muon_status muon_adamw_step(muon_handle *h, const muon_adamw_tensor *tensors, int32_t n,
+                            const muon_adamw_hparams *hp, void *stream);
 
 /* Frobenius norms ||u||_F of the orthogonalised inputs of the most recent
  * muon_step, one per plan entry (a blocked matrix has one per block, row-major)

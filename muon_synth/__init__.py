@@ -6,7 +6,13 @@ the optimizer's arithmetic lives here.
 """
 
 from .gen import (  # noqa: F401
+    ADAMW_WORKLOADS,
     WORKLOADS,
+    AdamWWorkload,
+    TensorSpec,
+    adamw_workload,
+    make_adamw_grad,
+    make_adamw_param,
     MatSpec,
     Workload,
     bf16_bits_to_f32,

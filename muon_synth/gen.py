@@ -298,3 +298,78 @@ def make_grad(wl: Workload, step: int, idx: int) -> np.ndarray:
 
 
 GradFn = Callable[[Workload, int, int], np.ndarray]
+
+
+# ---------------------------------------------------------------------------
+# AdamW parameter sets: the tensors the hybrid setup keeps off Muon
+# (embeddings, output head, norm gains and biases), as flat element counts.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class TensorSpec:
+    numel: int
+    name: str
+    kind: str = "weight"       # "weight" (N(0, 0.02^2)), "gain" (ones), "bias" (zeros)
+
+
+@dataclass(frozen=True)
+class AdamWWorkload:
+    name: str
+    wid: int
+    tensors: Tuple[TensorSpec, ...]
+    storage: str = "bf16"       # param / grad storage; both moments are float32
+    steps: int = 10
+    lr: float = 3e-3
+    beta1: float = 0.9
+    beta2: float = 0.95
+    eps: float = 1e-10
+    weight_decay: float = 0.0
+    grad_std_range: Tuple[float, float] = (-5.0, -2.0)   # log10 of the per-tensor gradient std
+    description: str = ""
+
+    @property
+    def elements(self) -> int:
+        return sum(t.numel for t in self.tensors)
+
+
+def _gpt2_adamw_set(layers: int, d: int, ff: int, vocab: int, ctx: int) -> Tuple[TensorSpec, ...]:
+    out: List[TensorSpec] = [TensorSpec(vocab * d, "wte"), TensorSpec(ctx * d, "wpe"),
+                             TensorSpec(vocab * d, "lm_head")]
+    for l in range(layers):
+        out += [TensorSpec(d, f"h{l}.ln1.g", "gain"), TensorSpec(d, f"h{l}.ln1.b", "bias"),
+                TensorSpec(3 * d, f"h{l}.attn.qkv.b", "bias"), TensorSpec(d, f"h{l}.attn.o.b", "bias"),
+                TensorSpec(d, f"h{l}.ln2.g", "gain"), TensorSpec(d, f"h{l}.ln2.b", "bias"),
+                TensorSpec(ff, f"h{l}.mlp.up.b", "bias"), TensorSpec(d, f"h{l}.mlp.down.b", "bias")]
+    out += [TensorSpec(d, "ln_f.g", "gain"), TensorSpec(d, "ln_f.b", "bias")]
+    return tuple(out)
+
+
+ADAMW_WORKLOADS: Dict[str, AdamWWorkload] = {
+    w.name: w
+    for w in (
+        AdamWWorkload("gpt2-124m-adamw-params", 20, _gpt2_adamw_set(12, 768, 3072, 50257, 1024),
+                      description="GPT-2 124M parameters off Muon: token embedding and untied head "
+                                  "(50257 x 768 each), position embedding 1024 x 768, norm gains and "
+                                  "biases, linear biases"),
+    )
+}
+
+
+def adamw_workload(name: str) -> AdamWWorkload:
+    return ADAMW_WORKLOADS[name]
+
+
+def make_adamw_param(wl: AdamWWorkload, idx: int) -> np.ndarray:
+    t = wl.tensors[idx]
+    if t.kind == "gain":
+        return np.ones(t.numel)
+    if t.kind == "bias":
+        return np.zeros(t.numel)
+    return rng_for(wl.wid, 0, idx, ROLE_PARAM).standard_normal(t.numel) * 0.02
+
+
+def make_adamw_grad(wl: AdamWWorkload, step: int, idx: int) -> np.ndarray:
+    """Gaussian gradient with a per-tensor scale, log-uniform over grad_std_range."""
+    lo, hi = wl.grad_std_range
+    std = 10.0 ** rng_for(wl.wid, 0, idx, ROLE_SCALE).uniform(lo, hi)
+    return rng_for(wl.wid, step, idx, ROLE_GRAD).standard_normal(wl.tensors[idx].numel) * std

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) Muon optimizer step behind a C ABI.
+"""MI355X (gfx950) Muon optimizer step (and the AdamW step of the hybrid
+setup's other parameters) behind a C ABI.
 
 The computation lives in ``libmuon_mi355x.so`` (hand-written HIP kernels);
 this package is its thin ctypes binding.  PyTorch supplies device memory and
@@ -20,10 +21,16 @@ from ._abi import (  # noqa: F401
     MUON_INIT_FAIL_ALLOC,
     MUON_INIT_PROFILE,
     MUON_OK,
+    AdamWHparams,
     Hparams,
     MuonError,
     load,
+    make_adamw_tensor,
     make_matrix,
+    muon_adamw_hparams,
+    muon_adamw_step,
+    muon_adamw_step_raw,
+    muon_adamw_tensor,
     muon_abi_version,
     muon_destroy,
     muon_init,

@@ -14,7 +14,7 @@ from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_mi355x.so")
-ABI_VERSION = 3   # the MUON_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 4   # the MUON_ABI_VERSION of the header this binding mirrors
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1
@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "muon_abi_version",
     "muon_init",
     "muon_step",
+    "muon_adamw_step",
     "muon_orthogonalize",
     "muon_read_norms",
     "muon_kernel_stats_read",
@@ -62,6 +63,29 @@ class muon_matrix(ctypes.Structure):
         ("block_rows", ctypes.c_int32),
         ("block_cols", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class muon_adamw_tensor(ctypes.Structure):
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class muon_adamw_hparams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("step", ctypes.c_int32),
     ]
 
 
@@ -113,6 +137,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_init.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_uint32]
     lib.muon_step.restype = ctypes.c_int
     lib.muon_step.argtypes = [vp, ctypes.POINTER(muon_matrix), i32, ctypes.POINTER(muon_hparams), vp]
+    lib.muon_adamw_step.restype = ctypes.c_int
+    lib.muon_adamw_step.argtypes = [vp, ctypes.POINTER(muon_adamw_tensor), i32, ctypes.POINTER(muon_adamw_hparams), vp]
     lib.muon_orthogonalize.restype = ctypes.c_int
     lib.muon_orthogonalize.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, ctypes.POINTER(muon_hparams), vp]
     lib.muon_read_norms.restype = ctypes.c_int
@@ -169,6 +195,19 @@ class Hparams:
             hp.coeffs = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
             hp._coeffs_keepalive = arr   # the array lives as long as the struct
         return hp
+
+
+@dataclass
+class AdamWHparams:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    step: int = 1              # 1-based step count of this update
+
+    def to_c(self) -> muon_adamw_hparams:
+        return muon_adamw_hparams(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, int(self.step))
 
 
 def _dtype_code(t) -> int:
@@ -232,6 +271,39 @@ def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp
     c_hp = hp.to_c()
     st = load().muon_step(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream))
     _check(handle, st)
+
+
+def make_adamw_tensor(param, grad, exp_avg, exp_avg_sq) -> muon_adamw_tensor:
+    """Describe one AdamW tensor (contiguous device tensors of equal size)."""
+    for t in (param, grad, exp_avg, exp_avg_sq):
+        if not t.is_contiguous():
+            raise ValueError("AdamW tensors must be contiguous")
+    n = int(param.numel())
+    if any(int(t.numel()) != n for t in (grad, exp_avg, exp_avg_sq)):
+        raise ValueError("param, grad, exp_avg and exp_avg_sq must have the same number of elements")
+    import torch
+    if exp_avg.dtype != torch.float32 or exp_avg_sq.dtype != torch.float32:
+        raise ValueError("exp_avg and exp_avg_sq are float32")
+    return muon_adamw_tensor(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), n,
+                             _dtype_code(param) if _dtype_code(param) == _dtype_code(grad) else -1, 0)
+
+
+def muon_adamw_step(handle: int, params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sqs: Sequence,
+                    hp: AdamWHparams, stream=None) -> None:
+    """One AdamW step over every (param, grad, exp_avg, exp_avg_sq) set, on ``stream``."""
+    n = len(params)
+    if len(grads) != n or len(exp_avgs) != n or len(exp_avg_sqs) != n:
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have the same length")
+    arr = (muon_adamw_tensor * max(n, 1))()
+    for i in range(n):
+        arr[i] = make_adamw_tensor(params[i], grads[i], exp_avgs[i], exp_avg_sqs[i])
+    c_hp = hp.to_c()
+    _check(handle, load().muon_adamw_step(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream)))
+
+
+def muon_adamw_step_raw(handle: int, arr, n: int, hp: muon_adamw_hparams, stream_ptr: int) -> int:
+    """Call with prepared ctypes arguments (the benchmark's inner loop); returns the status."""
+    return load().muon_adamw_step(handle, arr, n, ctypes.byref(hp), stream_ptr)
 
 
 def muon_step_raw(handle: int, arr, n: int, hp: muon_hparams, stream_ptr: int) -> int:

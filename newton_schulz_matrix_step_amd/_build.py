@@ -21,7 +21,7 @@ LIB_NAME = "libmuon_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["muon_api.cpp", "muon_kernels.hip"]
+SOURCES = ["muon_api.cpp", "muon_kernels.hip", "adamw_kernels.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -31,10 +31,12 @@ enum KernelRole {
     K_AXPY_LAST,
     K_DIRECT,
     K_FILL,
+    K_ADAMW,
     K_NROLES
 };
 const char* const kRoleNames[K_NROLES] = {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
-                                          "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero"};
+                                          "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero",
+                                          "adamw"};
 
 constexpr int kStageSlots = 4;
 constexpr int kMaxNsSteps = 64;
@@ -79,6 +81,23 @@ struct Plan {
     int slot = 0;
 };
 
+// AdamW: chunk table (static per list of sizes and dtypes) and the last
+// descriptor table sent to the device.
+struct AdamPlan {
+    bool valid = false;
+    std::vector<int64_t> key;
+    int n = 0;
+    AdamDesc* d_desc = nullptr;
+    AdamChunk* d_chunks = nullptr;
+    int n_chunks = 0;
+    std::vector<AdamDesc> uploaded;
+    bool have_uploaded = false;
+    AdamDesc* h_stage[kStageSlots] = {};
+    hipEvent_t stage_ev[kStageSlots] = {};
+    bool stage_used[kStageSlots] = {};
+    int slot = 0;
+};
+
 struct Pending {
     int role;
     hipEvent_t a, b;
@@ -91,6 +110,7 @@ struct muon_handle {
     uint32_t flags = 0;
     std::string err;
     Plan step_plan, ortho_plan;
+    AdamPlan adam_plan;
     bool profile = false;
     std::vector<Pending> pending;
     std::vector<hipEvent_t> ev_pool;
@@ -128,6 +148,16 @@ struct DeviceGuard {
         if (old >= 0) (void)hipSetDevice(old);
     }
 };
+
+void free_adam_plan(AdamPlan& p) {
+    (void)hipFree(p.d_desc);
+    (void)hipFree(p.d_chunks);
+    for (int i = 0; i < kStageSlots; ++i) {
+        if (p.stage_ev[i]) (void)hipEventDestroy(p.stage_ev[i]);
+        if (p.h_stage[i]) (void)hipHostFree(p.h_stage[i]);
+    }
+    p = AdamPlan();
+}
 
 void free_plan(Plan& p) {
     (void)hipFree(p.d_desc);
@@ -629,6 +659,145 @@ muon_status muon_orthogonalize(muon_handle* h, const void* in, float* out, int64
     return run(h, h->ortho_plan, m, hp, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+
+muon_status build_adam_plan(muon_handle* h, AdamPlan& p, const muon_adamw_tensor* ts, int n,
+                            const std::vector<int64_t>& key, hipStream_t stream) {
+    if (p.valid || p.d_desc) {
+        hipError_t e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize before re-plan");
+        free_adam_plan(p);
+    }
+    std::vector<AdamChunk> chunks;
+    for (int t = 0; t < n; ++t)
+        for (int64_t b = 0; b < ts[t].numel; b += kAdamChunk) chunks.push_back(AdamChunk{t, 0, b});
+    if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
+    AdamPlan q;
+    bool ok = hipMalloc(reinterpret_cast<void**>(&q.d_desc), sizeof(AdamDesc) * size_t(n)) == hipSuccess &&
+              hipMalloc(reinterpret_cast<void**>(&q.d_chunks), sizeof(AdamChunk) * std::max<size_t>(chunks.size(), 1)) ==
+                  hipSuccess;
+    for (int i = 0; ok && i < kStageSlots; ++i)
+        ok = hipHostMalloc(reinterpret_cast<void**>(&q.h_stage[i]), sizeof(AdamDesc) * size_t(n), hipHostMallocDefault) ==
+                 hipSuccess &&
+             hipEventCreateWithFlags(&q.stage_ev[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        (void)hipGetLastError();
+        free_adam_plan(q);
+        return fail(h, MUON_ERR_OOM, "AdamW plan allocation failed");
+    }
+    hipError_t e = hipSuccess;
+    if (!chunks.empty()) {
+        e = hipMemcpyAsync(q.d_chunks, chunks.data(), sizeof(AdamChunk) * chunks.size(), hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);   // the host vector dies with this call
+    }
+    if (e != hipSuccess) {
+        free_adam_plan(q);
+        return hip_fail(h, e, "AdamW plan upload");
+    }
+    q.n = n;
+    q.n_chunks = int(chunks.size());
+    q.key = key;
+    q.valid = true;
+    p = std::move(q);
+    return MUON_OK;
+}
+
+}  // namespace
+
+muon_status muon_adamw_step(muon_handle* h, const muon_adamw_tensor* ts, int32_t n, const muon_adamw_hparams* hp,
+                            void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    h->err.clear();
+    if (n < 0) return fail(h, MUON_ERR_INVALID_ARG, "n %d < 0", n);
+    if (n == 0) return MUON_OK;
+    if (!ts) return fail(h, MUON_ERR_INVALID_ARG, "tensors is NULL");
+    if (!hp) return fail(h, MUON_ERR_INVALID_ARG, "hparams is NULL");
+    if (!std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay) || !std::isfinite(hp->eps) || !(hp->eps > 0.f))
+        return fail(h, MUON_ERR_INVALID_ARG, "lr, weight_decay must be finite and eps finite and > 0");
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+        return fail(h, MUON_ERR_INVALID_ARG, "beta1, beta2 must lie in [0, 1)");
+    if (hp->step < 1) return fail(h, MUON_ERR_INVALID_ARG, "step %d < 1", hp->step);
+    int64_t chunks = 0;
+    for (int i = 0; i < n; ++i) {
+        const muon_adamw_tensor& t = ts[i];
+        if (t.reserved != 0) return fail(h, MUON_ERR_INVALID_ARG, "tensor %d: reserved field must be 0", i);
+        if (t.dtype != MUON_BF16 && t.dtype != MUON_F32) return fail(h, MUON_ERR_DTYPE, "tensor %d: unknown dtype %d", i, t.dtype);
+        if (t.numel < 0) return fail(h, MUON_ERR_INVALID_ARG, "tensor %d: numel %lld < 0", i, (long long)t.numel);
+        if (t.numel == 0) continue;
+        if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq)
+            return fail(h, MUON_ERR_INVALID_ARG, "tensor %d: a buffer is NULL", i);
+        const void* b[4] = {t.param, t.grad, t.exp_avg, t.exp_avg_sq};
+        for (int x = 0; x < 4; ++x)
+            for (int y = x + 1; y < 4; ++y)
+                if (b[x] == b[y]) return fail(h, MUON_ERR_INVALID_ARG, "tensor %d: two buffers alias", i);
+        chunks += (t.numel + kAdamChunk - 1) / kAdamChunk;
+        if (chunks > int64_t(INT32_MAX)) return fail(h, MUON_ERR_INVALID_ARG, "more than 2^31 - 1 chunks of %d elements", kAdamChunk);
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::vector<int64_t> key;
+    key.reserve(1 + 2 * size_t(n));
+    key.push_back(n);
+    for (int i = 0; i < n; ++i) {
+        key.push_back(ts[i].numel);
+        key.push_back(ts[i].dtype);
+    }
+    AdamPlan& plan = h->adam_plan;
+    if (!plan.valid || plan.key != key) {
+        muon_status st = build_adam_plan(h, plan, ts, n, key, s);
+        if (st != MUON_OK) return st;
+    }
+    std::vector<AdamDesc> desc(static_cast<size_t>(n));
+    for (int i = 0; i < n; ++i) {
+        const muon_adamw_tensor& t = ts[i];
+        AdamDesc& d = desc[size_t(i)];
+        std::memset(&d, 0, sizeof d);
+        d.param = t.param;
+        d.grad = t.grad;
+        d.m = t.exp_avg;
+        d.v = t.exp_avg_sq;
+        d.numel = t.numel;
+        d.dtype = t.dtype;
+        const uintptr_t pa = t.dtype == MUON_BF16 ? 8 : 16;   // bytes of 4 param/grad elements
+        auto al = [](const void* q, uintptr_t b) { return (reinterpret_cast<uintptr_t>(q) % b) == 0; };
+        d.vec = al(t.param, pa) && al(t.grad, pa) && al(t.exp_avg, 16) && al(t.exp_avg_sq, 16);
+    }
+    hipError_t e;
+    if (!plan.have_uploaded || std::memcmp(desc.data(), plan.uploaded.data(), sizeof(AdamDesc) * size_t(n)) != 0) {
+        const int sl = plan.slot;
+        if (plan.stage_used[sl]) {
+            e = hipEventSynchronize(plan.stage_ev[sl]);
+            if (e != hipSuccess) return hip_fail(h, e, "AdamW descriptor staging wait");
+        }
+        std::memcpy(plan.h_stage[sl], desc.data(), sizeof(AdamDesc) * size_t(n));
+        e = hipMemcpyAsync(plan.d_desc, plan.h_stage[sl], sizeof(AdamDesc) * size_t(n), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipEventRecord(plan.stage_ev[sl], s);
+        if (e != hipSuccess) return hip_fail(h, e, "AdamW descriptor upload");
+        plan.stage_used[sl] = true;
+        plan.slot = (sl + 1) % kStageSlots;
+        plan.uploaded = desc;
+        plan.have_uploaded = true;
+    }
+    // bias corrections in double, then the per-call constants in float
+    const double bc1 = 1.0 - std::pow(double(hp->beta1), double(hp->step));
+    const double bc2 = 1.0 - std::pow(double(hp->beta2), double(hp->step));
+    AdamArgs a;
+    a.beta1 = hp->beta1;
+    a.one_minus_beta1 = float(1.0 - double(hp->beta1));
+    a.beta2 = hp->beta2;
+    a.one_minus_beta2 = float(1.0 - double(hp->beta2));
+    a.decay = float(1.0 - double(hp->lr) * double(hp->weight_decay));
+    a.step_size = float(double(hp->lr) / bc1);
+    a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
+    a.eps = hp->eps;
+    e = timed(h, K_ADAMW, [&](hipEvent_t e0, hipEvent_t e1) {
+        return launch_adamw(plan.d_chunks, plan.n_chunks, plan.d_desc, a, s, e0, e1);
+    });
+    if (e != hipSuccess) return hip_fail(h, e, "adamw launch");
+    return MUON_OK;
+}
+
 muon_status muon_read_norms(muon_handle* h, float* out, int32_t n, void* stream) {
     if (!h || !out || n < 0) return MUON_ERR_INVALID_ARG;
     if (!h->step_plan.valid || n > h->step_plan.n) return fail(h, MUON_ERR_INVALID_ARG, "no step with %d matrices yet", n);
@@ -687,6 +856,7 @@ muon_status muon_destroy(muon_handle* h) {
         (void)hipDeviceSynchronize();
         free_plan(h->step_plan);
         free_plan(h->ortho_plan);
+        free_adam_plan(h->adam_plan);
         for (const Pending& p : h->pending) {
             (void)hipEventDestroy(p.a);
             (void)hipEventDestroy(p.b);

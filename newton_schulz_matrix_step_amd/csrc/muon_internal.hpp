@@ -83,6 +83,38 @@ hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* til
 hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* mats,
                                 PhaseArgs a, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+// ---- AdamW step (adamw_kernels.hip) ----
+// Elements per workgroup: a tensor of the call is cut into chunks of this many
+// elements (the last one ragged); one chunk table entry per chunk.
+constexpr int kAdamChunk = 4096;
+
+struct AdamDesc {
+    void* param;
+    const void* grad;
+    float* m;
+    float* v;
+    int64_t numel;
+    int32_t dtype;             // 0 bf16, 1 f32 (param and grad)
+    int32_t vec;               // bases allow 4-element vectors
+};
+
+struct AdamChunk {
+    int32_t t;                 // tensor index
+    int32_t pad;
+    int64_t begin;             // first element; the chunk ends at min(begin + kAdamChunk, numel)
+};
+
+struct AdamArgs {
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float decay;               // 1 - lr * weight_decay
+    float step_size;           // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;        // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+
+hipError_t launch_adamw(const AdamChunk* chunks, int n_chunks, const AdamDesc* tensors, AdamArgs a, hipStream_t s,
+                        hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+
 // Tile edge of the Newton-Schulz GEMMs (both modes use 128 x 128 tiles).
 constexpr int kTileF32 = 128;
 constexpr int kTileBf16 = 128;

@@ -107,3 +107,24 @@ def test_hparams_coeffs_marshalling():
         nsm.Hparams(ns_steps=3, coeffs=sched[:2]).to_c()  # fewer triples than iterations
     with pytest.raises(ValueError):
         nsm.Hparams(ns_steps=1, coeffs=[(1.0, 2.0)]).to_c()
+
+
+def test_adamw_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout_adamw.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "muon.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(muon_adamw_tensor), sizeof(muon_adamw_hparams),"
+        " offsetof(muon_adamw_tensor, numel), offsetof(muon_adamw_tensor, dtype), offsetof(muon_adamw_hparams, step));"
+        " return 0;}\n")
+    exe = tmp_path / "layout_adamw"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert out == [ctypes.sizeof(_abi.muon_adamw_tensor), ctypes.sizeof(_abi.muon_adamw_hparams),
+                   _abi.muon_adamw_tensor.numel.offset, _abi.muon_adamw_tensor.dtype.offset,
+                   _abi.muon_adamw_hparams.step.offset]
+
+
+def test_adamw_hparams_marshalling():
+    c = nsm.AdamWHparams(lr=0.25, beta1=0.5, beta2=0.75, eps=1e-6, weight_decay=0.125, step=7).to_c()
+    assert (c.lr, c.beta1, c.beta2, c.weight_decay, c.step) == (0.25, 0.5, 0.75, 0.125, 7)
+    assert c.eps == pytest.approx(1e-6, rel=1e-7)
