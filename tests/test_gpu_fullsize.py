@@ -141,3 +141,50 @@ def test_extreme_aspect_ratios():
             assert ok.all(), f"{r}x{c}: {int((~ok).sum())} weights beyond 1 bf16 ulp"
     finally:
         nsm.muon_destroy(h)
+
+
+@pytest.mark.gpu
+def test_maximum_dimension_vectors():
+    """The largest accepted dimension (2^20) as a single row and as a single
+    column, grouped in one call, plus the rejection of one more."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    from muon_synth.gen import MatSpec
+
+    big = 1 << 20
+    shapes = [(1, big), (big, 1)]
+    wl = workload("gpt2-124m-hidden")
+    wl = wl.with_(mats=tuple(MatSpec(r, c, f"v{i}") for i, (r, c) in enumerate(shapes)), steps=1, wid=77)
+    hp = hparams_for(wl)
+    ohp = oracle_hyper(wl)
+    h = nsm.muon_init(0)
+    try:
+        w_st = [encode_storage(make_param(wl, i), "bf16") for i in range(2)]
+        g_st = [encode_storage(make_grad(wl, 1, i), "bf16") for i in range(2)]
+        params = [to_device(x) for x in w_st]
+        grads = [to_device(x) for x in g_st]
+        moms = [torch.zeros(r, c, dtype=torch.float32, device="cuda") for r, c in shapes]
+        upd = [torch.empty(r, c, dtype=torch.float32, device="cuda") for r, c in shapes]
+        nsm.muon_step(h, params, grads, moms, hp, update_outs=upd)
+        torch.cuda.synchronize()
+        for i, (r, c) in enumerate(shapes):
+            w0 = oracle.decode(w_st[i])
+            res = oracle.muon_step_matrix(w0, oracle.decode(g_st[i]), np.zeros((r, c)), ohp)
+            o_gpu = to_stored(upd[i]).astype(np.float64)
+            e_o = relf(o_gpu, res.o)
+            print(f"  {r}x{c}: O rel err {e_o:.3e}", flush=True)
+            assert e_o <= TOL_O_BF16
+            sc = math.sqrt(max(1.0, r / c))
+            ok = weight_error_ok(to_stored(params[i]), w0, o_gpu, wl.lr, wl.weight_decay, sc)
+            assert ok.all()
+        # one more than the largest dimension is rejected before any work
+        g = torch.ones(1, big + 1, dtype=torch.bfloat16, device="cuda")
+        w = torch.zeros_like(g)
+        m = torch.zeros(1, big + 1, device="cuda")
+        with pytest.raises(nsm.MuonError) as ei:
+            nsm.muon_step(h, [w], [g], [m], hp)
+        assert ei.value.status == nsm.MUON_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert float(w.float().abs().max()) == 0.0 and float(m.abs().max()) == 0.0
+    finally:
+        nsm.muon_destroy(h)

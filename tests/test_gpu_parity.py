@@ -268,3 +268,16 @@ def test_invalid_block_rejected(block):
         assert float(w.abs().max()) == 0.0 and float(m.abs().max()) == 0.0
     finally:
         nsm.muon_destroy(h)
+
+
+def test_all_options_together():
+    """Blocks, a coefficient schedule, Nesterov, weight decay and float32
+    storage in one grouped call with plain matrices."""
+    shapes = [(256, 192), (192, 640), (130, 60), (77, 33)]
+    blocks = ((64, 0), (0, 128), (65, 0), (0, 0))
+    wl = _wl("allopts", shapes, steps=2, nesterov=True, weight_decay=0.05, storage="fp32",
+             coeffs=MIXED_SCHEDULE, blocks=blocks)
+    rep = []
+    rec = run_gpu(wl, 2, list(range(len(shapes))))
+    check_against_oracle(wl, rec, TOL_O_BF16, report=rep)
+    print("all options worst O rel err", max(e for (_, _, _, e) in rep))
