@@ -44,6 +44,12 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxEntries = 65536;   // plan entries (matrices or blocks) per muon_step call
 constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
+// Tile rows per item of the tile lists (see build_list): GRAM / POLY items of
+// 8 rows; an AXPY output of at most 8 tile rows is one item, taller ones go in
+// items of 4 rows (8 measured slower there).
+constexpr int kItemRowsSym = 8;
+constexpr int kItemRowsAxpyWhole = 8;
+constexpr int kItemRowsAxpy = 4;
 
 
 
@@ -325,7 +331,8 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
     // Tile lists.  Workgroup b runs on XCD b % 8, and each XCD has its own L2,
     // so every list is 8 chunks, one per XCD: chunk x holds the tiles XCD x
     // runs, in dispatch order.  Tiles come in items (one matrix's group of up
-    // to 4 tile rows across all tile columns, which share operand panels);
+    // to 4 or 8 tile rows across all tile columns, which share operand panels;
+    // within an item the rows of one column are consecutive);
     // items are dealt to the XCDs largest first, each to the least-loaded one
     // (load = tiles x k blocks), so every XCD gets about the same work however
     // mixed the matrix shapes (keeping a matrix on one XCD for L2 reuse
@@ -349,12 +356,14 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
             tm = sym ? (d.m + T - 1) / T : (d.R + T - 1) / T;
             tn = sym ? tm : (d.C + T - 1) / T;
         };
+        auto item_rows = [&](int tm) { return sym ? kItemRowsSym : (tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy); };
         for (int i = 0; i < n; ++i) {
             int tm, tn;
             dims(geom[i], tm, tn);
-            for (int a0 = 0; a0 < tm; a0 += 4) {
+            const int IR = item_rows(tm);
+            for (int a0 = 0; a0 < tm; a0 += IR) {
                 int64_t cnt = 0;
-                for (int a = a0; a < std::min(tm, a0 + 4); ++a) cnt += sym ? tn - a : tn;
+                for (int a = a0; a < std::min(tm, a0 + IR); ++a) cnt += sym ? tn - a : tn;
                 items.push_back(Item{i, a0, cnt * ksteps(geom[i])});
             }
         }
@@ -368,8 +377,9 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
             load[x] += it.w;
             int tm, tn;
             dims(geom[it.mat], tm, tn);
+            const int IR = item_rows(tm);
             for (int b = 0; b < tn; ++b)
-                for (int a = it.a0; a < std::min(tm, it.a0 + 4); ++a)
+                for (int a = it.a0; a < std::min(tm, it.a0 + IR); ++a)
                     if (!sym || b >= a) bins[x].push_back(Tile{it.mat, a, b, 0});
         }
         size_t chunk = 0;
