@@ -28,6 +28,8 @@ COMMON_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    "-fvisibility=hidden",
+    "-fvisibility-inlines-hidden",
     "-Wall",
     "-Wno-unused-function",
     # no packed-fp32 instructions in generated code

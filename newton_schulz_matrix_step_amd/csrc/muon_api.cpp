@@ -15,7 +15,10 @@
 #include <string>
 #include <vector>
 
+// the library is built with hidden visibility: only the C ABI is exported
+#pragma GCC visibility push(default)
 #include "../../include/muon.h"
+#pragma GCC visibility pop
 #include "muon_internal.hpp"
 
 using namespace muon;

@@ -7,7 +7,7 @@
 //                       iteration, grouped over every matrix of the call:
 //                         GRAM  A = X X^T           (upper tiles, mirrored store)
 //                         POLY  B = b A + c A A     (A symmetric: A A = A A^T)
-//                         AXPY  X' = a X + B X      (master X as bf16 hi + lo)
+//                         AXPY  X' = a X + B X      (master X: bf16 hi + 8-bit lo)
 //                         AXPY_LAST  same, then W' = W (1 - lr wd) - lr s O
 //  ns_gemm_kernel<KIND> the same phases in fp32 (validation mode)
 //  direct_update        the update when ns_steps == 0

@@ -37,6 +37,16 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(declared) == sorted(_abi.EXPORTED_SYMBOLS)
 
 
+def test_only_the_c_abi_is_exported(lib):
+    """Every exported muon_* function is declared in the header, and no
+    internal (C++ namespace) symbol of the library leaks out."""
+    out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout.split("\n")
+    names = [l.split()[-1] for l in out if len(l.split()) == 3 and l.split()[1] in ("T", "W")]
+    assert sorted(n for n in names if n.startswith("muon_")) == _declared_functions()
+    assert not [n for n in names if "4muon" in n and not n.startswith("_ZNSt")]
+
+
 def test_abi_version(lib):
     text = open(HEADER).read()
     ver = int(re.search(r"#define MUON_ABI_VERSION (\d+)", text).group(1))
