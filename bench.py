@@ -64,7 +64,7 @@ def algorithmic_work(wl):
     """
     gb = 2 if wl.storage == "bf16" else 4
     ub = 2 if wl.compute == "bf16" else 4
-    gram = poly = axpy = 0
+    gram = poly = axpy = dense = 0
     elems = 0
     for i, s in enumerate(wl.mats):
         for (r, c) in block_shapes(wl, i):
@@ -72,10 +72,12 @@ def algorithmic_work(wl):
             gram += m * (m + 1) * n
             poly += m * m * (m + 1)
             axpy += 2 * m * m * n
+            dense += 4 * m * m * n + 2 * m ** 3
         elems += s.rows * s.cols
     return {
         "flops": {"ns_gram": gram, "ns_poly": poly, "ns_axpy": axpy, "ns_axpy_update": axpy},
         "ns_flops_per_step": wl.ns_steps * (gram + poly + axpy),
+        "ns_dense_flops_per_step": wl.ns_steps * dense,   # the pages' convention, 4 m^2 n + 2 m^3 an iteration
         "momentum_bytes": elems * (gb + 4 + 4 + ub),
         "elements": elems,
     }
@@ -173,45 +175,56 @@ def cpu_baseline(wl, grads_host, budget_s: float):
         cores = os.cpu_count() or 1
     hp = oracle.Hyper(lr=wl.lr, beta=wl.beta, weight_decay=wl.weight_decay, nesterov=wl.nesterov,
                       ns_steps=wl.ns_steps, eps=wl.eps, a=wl.a, b=wl.b, c=wl.c, coeffs=wl.coeffs)
-    # whole passes over the matrix list (step 1's inputs) while the budget
-    # lasts; a pass that alone exceeds it stops early and is extrapolated
-    done_elems, t_used, k, passes = 0, 0.0, 0, 0
-    total = sum(s.rows * s.cols for s in wl.mats)
     weights = [sum(min(r, c) ** 2 * (2 * max(r, c) + min(r, c)) for (r, c) in block_shapes(wl, i))
                for i in range(len(wl.mats))]
-    done_flops = 0
-    while t_used < budget_s:
-        w = oracle.decode(grads_host["param"][k])
-        g = oracle.decode(grads_host["grad0"][k])
-        m = np.asarray(make_momentum(wl, k), dtype=np.float64)
-        t0 = time.perf_counter()
-        if block_of(wl, k) == (0, 0):
-            oracle.muon_step_matrix(w, g, m, hp)
+    total = sum(s.rows * s.cols for s in wl.mats)
+
+    def run(budget):
+        # whole passes over the matrix list (step 1's inputs) while the budget
+        # lasts; a pass that alone exceeds it stops early and is extrapolated
+        done_elems, t_used, k, passes, done_flops = 0, 0.0, 0, 0, 0
+        while t_used < budget:
+            w = oracle.decode(grads_host["param"][k])
+            g = oracle.decode(grads_host["grad0"][k])
+            m = np.asarray(make_momentum(wl, k), dtype=np.float64)
+            t0 = time.perf_counter()
+            if block_of(wl, k) == (0, 0):
+                oracle.muon_step_matrix(w, g, m, hp)
+            else:
+                oracle.muon_step_matrix_blocked(w, g, m, hp, *block_of(wl, k))
+            t_used += time.perf_counter() - t0
+            done_elems += wl.mats[k].rows * wl.mats[k].cols
+            done_flops += weights[k]
+            k += 1
+            if k == len(wl.mats):
+                k = 0
+                passes += 1
+        # extrapolate by Newton-Schulz flops (the oracle's cost is its dgemms)
+        est_step_s = t_used * sum(weights) / max(done_flops, 1)
+        if passes:
+            what = f"{passes} full step(s) over all {len(wl.mats)} matrices"
+            if k:
+                what += f" plus {k} matrices"
         else:
-            oracle.muon_step_matrix_blocked(w, g, m, hp, *block_of(wl, k))
-        t_used += time.perf_counter() - t0
-        done_elems += wl.mats[k].rows * wl.mats[k].cols
-        done_flops += weights[k]
-        k += 1
-        if k == len(wl.mats):
-            k = 0
-            passes += 1
-    # extrapolate by Newton-Schulz flops (the oracle's cost is its dgemms)
-    est_step_s = t_used * sum(weights) / max(done_flops, 1)
-    if passes:
-        what = f"{passes} full step(s) over all {len(wl.mats)} matrices"
-        if k:
-            what += f" plus {k} matrices"
-    else:
-        what = f"{k} of {len(wl.mats)} matrices of one step ({done_elems}/{total} elements)"
-    return {
-        "value": 1.0 / est_step_s,
+            what = f"{k} of {len(wl.mats)} matrices of one step ({done_elems}/{total} elements)"
+        return est_step_s, f"{what} with step 1's inputs, {t_used:.1f} s of float64 NumPy/OpenBLAS"
+
+    est, what = run(budget_s)
+    out = {
+        "value": 1.0 / est,
         "unit": "steps/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": f"{what} with step 1's inputs, {t_used:.1f} s of float64 NumPy/OpenBLAS; "
-                  "steps/s = Newton-Schulz flops of one step / flops done per second",
+        "sample": what + "; steps/s = Newton-Schulz flops of one step / flops done per second",
     }
+    try:   # the same oracle on one thread, over a shorter sample
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            est1, what1 = run(min(4.0, budget_s))
+        out["one_thread"] = {"value": 1.0 / est1, "cores": 1, "sample": what1}
+    except Exception as e:  # pragma: no cover
+        out["one_thread"] = {"value": None, "error": str(e)}
+    return out
 
 
 def adamw_bench(args):
@@ -432,14 +445,21 @@ def main():
     nsm.muon_destroy(h)
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # ---- the same steps on a plain handle (no events), for comparison ----
+    # ---- the same steps on a plain handle (no per-kernel events), for
+    # comparison, each step bracketed by events on the launch stream for the
+    # distribution of step times ----
     h = nsm.muon_init(0)
     run_steps(h, args.warmup, 0)
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    run_steps(h, args.steps, args.warmup)
+    evs[0].record(stream)
+    for j in range(args.steps):
+        run_steps(h, 1, args.warmup + j)
+        evs[j + 1].record(stream)
     torch.cuda.synchronize()
     plain_ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_ms = np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps)])
     nsm.muon_destroy(h)
 
     kernels = {}
@@ -483,6 +503,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_no_events": round(plain_ms_per_step, 4),
+        "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -500,6 +521,7 @@ def main():
             "weight_decay": wl.weight_decay,
         },
         "ns_tflops": round(ns_tflops, 2),
+        "ns_tflops_dense_equiv": round(work["ns_dense_flops_per_step"] / (ns_ms * 1e-3) / 1e12, 2) if ns_ms > 0 else 0.0,
         "ns_frac_peak": round(ns_tflops / peak, 4),
         "ns_ms_per_step": round(ns_ms, 4),
         "momentum_hbm_frac": round(mom.get("gbs", 0.0) / PEAK_HBM_GBS, 4) if mom else None,
