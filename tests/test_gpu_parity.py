@@ -281,3 +281,59 @@ def test_all_options_together():
     rec = run_gpu(wl, 2, list(range(len(shapes))))
     check_against_oracle(wl, rec, TOL_O_BF16, report=rep)
     print("all options worst O rel err", max(e for (_, _, _, e) in rep))
+
+
+def _phi5_scalar(x, a=3.4445, b=-4.7750, c=2.0315):
+    """Five applications of the scalar quintic a x + b x^3 + c x^5 (pure Python)."""
+    for _ in range(5):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+@pytest.mark.parametrize("compute", ["fp32", "bf16"])
+def test_degenerate_inputs_against_closed_forms(compute):
+    """Independent of the oracle.
+
+    Rank one: u v^T comes out as phi_5(s/(s+eps)) u v^T / s (s = |u||v|).  The
+    coefficient along u v^T must match (fp32 1e-6, bf16 1e-3 relative); the
+    whole matrix carries the rounding noise of the null space, which every
+    finite-precision Newton-Schulz amplifies by the quintic's slope at 0
+    (3.4445 an iteration, ~486 over five): fp32 bar 5e-4 (measured 1.4e-4),
+    bf16 the usual 3e-2 (measured 2.9e-3).
+    Orthonormal rows scaled by c (64 x 640 and its transpose): phi_5(c/(c
+    sqrt(64) + eps)) times the input over c; full rank, so the usual bars
+    (fp32 1e-5, measured 4.7e-7; bf16 3e-2, measured 1.5e-2).
+    """
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    rng = np.random.default_rng(21)
+    fp32 = compute == "fp32"
+
+    def ortho(g):
+        gin = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda()
+        out = torch.empty_like(gin)
+        nsm.muon_orthogonalize(h, gin, out, nsm.Hparams(compute=compute))
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    h = nsm.muon_init(0)
+    try:
+        u, v = rng.standard_normal(256), rng.standard_normal(384)
+        g = np.outer(u, v) * 1e-3
+        s = np.linalg.norm(g)
+        k = _phi5_scalar(s / (s + 1e-7))
+        o = ortho(g)
+        coef = float(np.sum(o * g) / s)
+        err = relf(o, k * g / s)
+        print(compute, "rank one: coefficient", coef, "closed form", k, f"matrix rel err {err:.2e}")
+        assert abs(coef - k) <= (1e-6 if fp32 else 1e-3) * k
+        assert err <= (5e-4 if fp32 else TOL_O_BF16)
+        q, _ = np.linalg.qr(rng.standard_normal((640, 64)))
+        g = np.ascontiguousarray(q.T) * 0.05
+        k = _phi5_scalar(0.05 / (0.05 * 8.0 + 1e-7))
+        for gi in (g, np.ascontiguousarray(g.T)):
+            err = relf(ortho(gi), k * gi / 0.05)
+            print(compute, "orthonormal", gi.shape, f"rel err {err:.2e}")
+            assert err <= (TOL_O_FP32 if fp32 else TOL_O_BF16)
+    finally:
+        nsm.muon_destroy(h)
