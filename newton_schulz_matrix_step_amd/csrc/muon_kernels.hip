@@ -56,7 +56,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // units of 1/256 of the bf16 spacing at hi (spacing 2^(E-134) for biased
 // exponent E >= 1, the denormal spacing for E = 0), rounded to nearest and
 // stored offset by 128.  The remainder of a round-to-nearest is at most half
-// a spacing, 128 units; hi + lo then holds x to 2^-16 relative.
+// a spacing, 128 units (clamped to 127); hi + lo then holds x to half a unit,
+// one unit at such ties: 2^-15 relative at worst.
 __device__ __forceinline__ int lo8_unit_exp(uint32_t hbits) {
     const int e = int((hbits >> 7) & 0xFFu);
     return (e < 1 ? 1 : e) - 142;
