@@ -337,3 +337,51 @@ def test_degenerate_inputs_against_closed_forms(compute):
             assert err <= (TOL_O_FP32 if fp32 else TOL_O_BF16)
     finally:
         nsm.muon_destroy(h)
+
+
+def test_save_reload_continue_is_bitwise_unbroken():
+    """Four steps in one run against two steps, a save of weights and momenta to
+    host memory, a reload into fresh buffers on a fresh handle and two more
+    steps: the library keeps no state between steps beyond its plan, so the
+    two must agree bit for bit."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    from muon_synth import make_grad, make_momentum, make_param, encode_storage
+    wl = _wl("resume", [(300, 100), (128, 384), (96, 96)], steps=4, nesterov=True, weight_decay=0.02)
+    n = len(wl.mats)
+    hp = nsm.Hparams(lr=wl.lr, weight_decay=wl.weight_decay, nesterov=True)
+    grads = {s: [to_device(encode_storage(make_grad(wl, s, i), "bf16")) for i in range(n)] for s in range(1, 5)}
+
+    def fresh():
+        return ([to_device(encode_storage(make_param(wl, i), "bf16")) for i in range(n)],
+                [to_device(encode_storage(make_momentum(wl, i), "fp32")) for i in range(n)])
+
+    def steps(h, ws, ms, s0, s1):
+        for s in range(s0, s1 + 1):
+            nsm.muon_step(h, ws, grads[s], ms, hp)
+        torch.cuda.synchronize()
+
+    h = nsm.muon_init(0)
+    try:
+        w_a, m_a = fresh()
+        steps(h, w_a, m_a, 1, 4)
+    finally:
+        nsm.muon_destroy(h)
+    h = nsm.muon_init(0)
+    try:
+        w_b, m_b = fresh()
+        steps(h, w_b, m_b, 1, 2)
+        saved = [(to_stored(w), m.cpu().numpy().copy()) for w, m in zip(w_b, m_b)]
+    finally:
+        nsm.muon_destroy(h)
+    del w_b, m_b
+    h = nsm.muon_init(0)
+    try:
+        w_c = [to_device(w) for w, _ in saved]
+        m_c = [to_device(m) for _, m in saved]
+        steps(h, w_c, m_c, 3, 4)
+    finally:
+        nsm.muon_destroy(h)
+    for i in range(n):
+        assert np.array_equal(to_stored(w_a[i]), to_stored(w_c[i]))
+        assert np.array_equal(m_a[i].cpu().numpy(), m_c[i].cpu().numpy())
