@@ -385,3 +385,28 @@ def test_save_reload_continue_is_bitwise_unbroken():
     for i in range(n):
         assert np.array_equal(to_stored(w_a[i]), to_stored(w_c[i]))
         assert np.array_equal(m_a[i].cpu().numpy(), m_c[i].cpu().numpy())
+
+
+def test_forced_allocation_failure():
+    """A handle created with MUON_INIT_FAIL_ALLOC fails every workspace or plan
+    allocation: both entry points report MUON_ERR_OOM and change nothing."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    h = nsm.muon_init(0, nsm.MUON_INIT_FAIL_ALLOC)
+    try:
+        g = torch.randn(64, 96, device="cuda")
+        w, m = torch.zeros_like(g), torch.zeros_like(g)
+        with pytest.raises(nsm.MuonError) as ei:
+            nsm.muon_step(h, [w], [g], [m], nsm.Hparams())
+        assert ei.value.status == nsm.MUON_ERR_OOM
+        p, gv = torch.zeros(1000, device="cuda"), torch.ones(1000, device="cuda")
+        mv, vv = torch.zeros(1000, device="cuda"), torch.zeros(1000, device="cuda")
+        with pytest.raises(nsm.MuonError) as ei:
+            nsm.muon_adamw_step(h, [p], [gv], [mv], [vv], nsm.AdamWHparams())
+        assert ei.value.status == nsm.MUON_ERR_OOM
+        torch.cuda.synchronize()
+        assert float(w.abs().max()) == 0.0 and float(m.abs().max()) == 0.0
+        assert float(p.abs().max()) == 0.0 and float(mv.abs().max()) == 0.0
+        assert nsm.muon_workspace_bytes(h) == 0
+    finally:
+        nsm.muon_destroy(h)
