@@ -26,7 +26,9 @@ constexpr int kAdamThreads = 256;
 constexpr int kRuns = kAdamChunk / (4 * kAdamThreads);   // runs of 4 elements per lane
 static_assert(kRuns * 4 * kAdamThreads == kAdamChunk, "chunk = lanes x runs x 4");
 
+#ifndef GMEM   // a host build for bounds checking defines it empty
 #define GMEM __attribute__((address_space(1)))
+#endif
 template <class T>
 __device__ __forceinline__ GMEM T* gm(T* p) { return (GMEM T*)p; }
 

@@ -40,7 +40,9 @@ constexpr int kThreads = 256;
 // accesses become flat instructions, which count against the LDS wait counter as
 // well: an epilogue that mixes them with LDS staging waits for its global loads
 // at every LDS wait.  gm() restates the address space.
+#ifndef GMEM   // a host build for bounds checking defines it empty
 #define GMEM __attribute__((address_space(1)))
+#endif
 template <class T>
 __device__ __forceinline__ GMEM T* gm(T* p) { return (GMEM T*)p; }
 

@@ -1,0 +1,86 @@
+// Test infrastructure: runs muon_step and muon_adamw_step of the library, built
+// against the CPU stand-in of HIP (tests/emu/hip), on exactly sized host
+// buffers, so AddressSanitizer reports any access outside a caller buffer or
+// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS]
+//   SHAPES "RxC,RxC,...", DTYPE 0 = bf16, 1 = f32 (also selects fp32 compute),
+//   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+
+emu_idx threadIdx, blockIdx;
+dim3 gridDim, blockDim;
+long emu_launches = 0;
+int emu_verbose = 0;
+
+int main(int argc, char** argv) {
+    if (argc < 4) return 2;
+    const std::string spec = argv[1];
+    const int ns = std::atoi(argv[2]);
+    const int dtype = std::atoi(argv[3]);
+    const int block_rows = argc > 4 ? std::atoi(argv[4]) : 0;
+    std::vector<std::pair<long, long>> shapes;
+    for (size_t p = 0; p < spec.size();) {
+        size_t q = spec.find(',', p);
+        const std::string t = spec.substr(p, q == std::string::npos ? std::string::npos : q - p);
+        shapes.push_back({std::atol(t.c_str()), std::atol(t.c_str() + t.find('x') + 1)});
+        if (q == std::string::npos) break;
+        p = q + 1;
+    }
+    const int es = dtype == 0 ? 2 : 4;
+    std::vector<muon_matrix> mats;
+    for (auto [r, c] : shapes) {
+        muon_matrix m{};
+        m.param = std::calloc(r * c, es);
+        m.grad = std::calloc(r * c, es);
+        m.momentum = static_cast<float*>(std::calloc(r * c, 4));
+        m.update_out = static_cast<float*>(std::calloc(r * c, 4));
+        m.rows = r;
+        m.cols = c;
+        m.ld_param = m.ld_grad = m.ld_mom = m.ld_update = c;
+        m.dtype = dtype;
+        if (block_rows > 0 && r % block_rows == 0) m.block_rows = block_rows;
+        mats.push_back(m);
+    }
+    muon_handle* h = nullptr;
+    if (muon_init(&h, 0, 0) != MUON_OK) return 3;
+    const float sched[6] = {3.4445f, -4.7750f, 2.0315f, 1.5f, -0.5f, 0.0f};
+    muon_hparams hp{0.02f, 0.95f, 0.01f, 1e-7f, 3.4445f, -4.775f, 2.0315f, 1, ns,
+                    dtype == 0 ? MUON_COMPUTE_BF16 : MUON_COMPUTE_FP32, ns == 2 ? sched : nullptr};
+    int st = muon_step(h, mats.data(), static_cast<int>(mats.size()), &hp, nullptr);
+    std::printf("step %d (%s) launches %ld\n", st, muon_last_error(h), emu_launches);
+    // AdamW over ragged sizes: vector path, ragged tail and scalar path
+    const long sizes[5] = {1, 4095, 4096, 4097, 10001};
+    std::vector<muon_adamw_tensor> ts;
+    for (long n : sizes) {
+        muon_adamw_tensor t{};
+        t.param = std::calloc(n, es);
+        t.grad = std::calloc(n, es);
+        t.exp_avg = static_cast<float*>(std::calloc(n, 4));
+        t.exp_avg_sq = static_cast<float*>(std::calloc(n, 4));
+        t.numel = n;
+        t.dtype = dtype;
+        ts.push_back(t);
+    }
+    muon_adamw_hparams ah{1e-3f, 0.9f, 0.999f, 1e-8f, 0.01f, 1};
+    const int st2 = muon_adamw_step(h, ts.data(), static_cast<int>(ts.size()), &ah, nullptr);
+    std::printf("adamw %d (%s)\n", st2, muon_last_error(h));
+    muon_destroy(h);
+    for (auto& m : mats) {
+        std::free(m.param);
+        std::free(const_cast<void*>(m.grad));
+        std::free(m.momentum);
+        std::free(m.update_out);
+    }
+    for (auto& t : ts) {
+        std::free(t.param);
+        std::free(const_cast<void*>(t.grad));
+        std::free(t.exp_avg);
+        std::free(t.exp_avg_sq);
+    }
+    return st != MUON_OK ? 4 : (st2 != MUON_OK ? 5 : 0);
+}
