@@ -60,7 +60,8 @@ typedef enum muon_dtype {
 } muon_dtype;
 
 typedef enum muon_compute {
-    MUON_COMPUTE_BF16 = 0,     /* bf16 MFMA operands, fp32 accumulation, fp32 master X */
+    MUON_COMPUTE_BF16 = 0,     /* bf16 MFMA operands, fp32 accumulation; X kept between iterations
+                                  to ~16 bits (bf16 copy + 8-bit remainder), A and B in bf16 */
     MUON_COMPUTE_FP32 = 1      /* fp32 MFMA operands and storage: validation mode */
 } muon_compute;
 
