@@ -22,7 +22,7 @@ import pytest
 import oracle
 from muon_synth import encode_storage, expert_scale, make_grad, make_momentum, make_param, workload
 
-from gpu_harness import (TOL_O_BF16, hparams_for, oracle_hyper, relf, to_device, to_stored,
+from gpu_harness import (TOL_O_BF16, hparams_for, oracle_hyper, relf, shape_scales, to_device, to_stored,
                          weight_error_ok)
 
 
@@ -39,6 +39,8 @@ CASES = [
     ("gpt2-350m-hidden", 2, (0, 4, 5, 143)),            # 1024^2, 1024x4096, 4096x1024, last matrix
     ("moe-64x-2048x1408", 2, None),
     ("large-layer-share-4096x14336", 1, (2, 9)),         # 14336x4096 (transposed, s = 1.871), 4096^2
+    # query and key in six 128x768 blocks (pairs of heads), value and the MLP whole
+    ("gpt2-124m-hidden-qk-head-pairs", 2, (0, 1, 2, 4, 5, 66)),
 ]
 
 
@@ -72,7 +74,7 @@ def _run_fullsize(name: str, steps: int, sample):
             m_old = [to_stored(m) for m in moms]
             w_old = {i: to_stored(params[i]) for i in sample}
             print(f"{name} step {s}: inputs ready in {time.perf_counter() - t0:.1f} s", flush=True)
-            nsm.muon_step(h, params, grads, moms, hp, update_outs=upd)
+            nsm.muon_step(h, params, grads, moms, hp, update_outs=upd, blocks=wl.blocks)
             torch.cuda.synchronize()
             for i in range(n):
                 got = to_stored(moms[i]).astype(np.float64)
@@ -81,7 +83,11 @@ def _run_fullsize(name: str, steps: int, sample):
             for i in sample:
                 t1 = time.perf_counter()
                 w0 = oracle.decode(w_old[i])
-                res = oracle.muon_step_matrix(w0, oracle.decode(g_st[i]), m_oracle[i], ohp)
+                blk = wl.blocks[i] if wl.blocks is not None else (0, 0)
+                if blk == (0, 0):
+                    res = oracle.muon_step_matrix(w0, oracle.decode(g_st[i]), m_oracle[i], ohp)
+                else:
+                    res = oracle.muon_step_matrix_blocked(w0, oracle.decode(g_st[i]), m_oracle[i], ohp, *blk)
                 o_gpu = to_stored(upd[i]).astype(np.float64)
                 e_o = relf(o_gpu, res.o)
                 worst = max(worst, e_o)
@@ -89,7 +95,7 @@ def _run_fullsize(name: str, steps: int, sample):
                 print(f"  matrix {i} {shape} step {s}: O rel err {e_o:.3e} "
                       f"(oracle {time.perf_counter() - t1:.1f} s)", flush=True)
                 assert e_o <= TOL_O_BF16, f"{name} matrix {i} step {s}: O rel err {e_o:.3e}"
-                sc = math.sqrt(max(1.0, shape[0] / shape[1]))
+                sc = shape_scales(shape, blk)
                 ok = weight_error_ok(to_stored(params[i]), w0, o_gpu, wl.lr, wl.weight_decay, sc)
                 assert ok.all(), f"{name} matrix {i} step {s}: {int((~ok).sum())} weights beyond 1 bf16 ulp"
                 m_oracle[i] = res.m
