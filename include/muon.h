@@ -66,8 +66,26 @@ typedef enum muon_compute {
 } muon_compute;
 
 /* init flags */
-#define MUON_INIT_PROFILE     0x1u   /* time every kernel launch with HIP events */
+#define MUON_INIT_PROFILE     0x1u   /* time kernel launches with HIP events (all roles, or see below) */
 #define MUON_INIT_FAIL_ALLOC  0x2u   /* test hook: every workspace allocation fails (MUON_ERR_OOM) */
+
+/* Kernel roles, as named in muon_kernel_stats.name. */
+typedef enum muon_role {
+    MUON_ROLE_MOMENTUM = 0,    /* "momentum_norm" */
+    MUON_ROLE_FINALIZE = 1,    /* "norm_finalize" */
+    MUON_ROLE_GRAM = 2,        /* "ns_gram" */
+    MUON_ROLE_POLY = 3,        /* "ns_poly" */
+    MUON_ROLE_AXPY = 4,        /* "ns_axpy" (every iteration but the last) */
+    MUON_ROLE_AXPY_UPDATE = 5, /* "ns_axpy_update" (last iteration and the weight update) */
+    MUON_ROLE_DIRECT = 6,      /* "direct_update" (ns_steps == 0) */
+    MUON_ROLE_FILL = 7,        /* "fill_zero" (workspace initialisation) */
+    MUON_ROLE_ADAMW = 8        /* "adamw" */
+} muon_role;
+
+/* With MUON_INIT_PROFILE, time only the roles whose bits are set in `mask`
+ * (bit r = role r); no bits = every role.  Each timed launch carries its own
+ * start/stop events, which costs a little time per launch. */
+#define MUON_INIT_PROFILE_ROLES(mask) ((((uint32_t)(mask)) & 0x1FFu) << 16)
 
 /* One weight matrix of the list handed to muon_step. */
 typedef struct muon_matrix {
@@ -141,7 +159,7 @@ typedef struct muon_adamw_hparams {
 int muon_abi_version(void);
 
 /* Create a handle on HIP device `device`.  *out receives the handle (NULL on error).
- * Errors: MUON_ERR_INVALID_ARG (out == NULL, device out of range, unknown flag bits),
+ * Errors: MUON_ERR_INVALID_ARG (out == NULL, device out of range, unknown flag or role bits),
  * MUON_ERR_NO_DEVICE (no HIP device visible). */
 muon_status muon_init(muon_handle **out, int device, uint32_t flags);
 
@@ -152,6 +170,9 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
  * signature allocate nothing.
  * A matrix cut into blocks (block_rows/block_cols) enters the plan as one entry
  * per block, in row-major block order; at most 65536 entries per call.
+ * A call with the same list of shapes and the same pointers as the handle's
+ * previous call enqueues kernel launches only (no allocation, copy or memset),
+ * so it may be captured into a HIP graph and replayed.
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
  * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
  * momentum aliasing param or grad, ns_steps outside 0..64, a == 0 or a non-finite

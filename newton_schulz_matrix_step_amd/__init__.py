@@ -21,6 +21,7 @@ from ._abi import (  # noqa: F401
     MUON_INIT_FAIL_ALLOC,
     MUON_INIT_PROFILE,
     MUON_OK,
+    ROLE_NAMES,
     AdamWHparams,
     Hparams,
     MuonError,
@@ -44,5 +45,6 @@ from ._abi import (  # noqa: F401
     muon_step,
     muon_step_raw,
     muon_workspace_bytes,
+    profile_roles,
     muon_hparams,
 )

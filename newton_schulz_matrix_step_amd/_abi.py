@@ -31,6 +31,19 @@ MUON_COMPUTE_FP32 = 1
 MUON_INIT_PROFILE = 0x1
 MUON_INIT_FAIL_ALLOC = 0x2
 
+# kernel roles (muon_role), named as in muon_kernel_stats
+ROLE_NAMES = ("momentum_norm", "norm_finalize", "ns_gram", "ns_poly", "ns_axpy", "ns_axpy_update",
+              "direct_update", "fill_zero", "adamw")
+
+
+def profile_roles(names) -> int:
+    """MUON_INIT_PROFILE_ROLES for the named roles: init flag bits that limit a
+    profiling handle's events to those roles."""
+    mask = 0
+    for nm in names:
+        mask |= 1 << ROLE_NAMES.index(nm)
+    return (mask & 0x1FF) << 16
+
 EXPORTED_SYMBOLS = (
     "muon_abi_version",
     "muon_init",

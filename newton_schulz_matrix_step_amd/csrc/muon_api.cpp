@@ -25,6 +25,7 @@ using namespace muon;
 
 namespace {
 
+// the order is the ABI's muon_role
 enum KernelRole {
     K_MOMENTUM = 0,
     K_FINALIZE,
@@ -37,6 +38,9 @@ enum KernelRole {
     K_ADAMW,
     K_NROLES
 };
+static_assert(K_MOMENTUM == MUON_ROLE_MOMENTUM && K_GRAM == MUON_ROLE_GRAM && K_AXPY == MUON_ROLE_AXPY &&
+                  K_AXPY_LAST == MUON_ROLE_AXPY_UPDATE && K_ADAMW == MUON_ROLE_ADAMW && K_NROLES == 9,
+              "kernel roles follow muon_role");
 const char* const kRoleNames[K_NROLES] = {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
                                           "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero",
                                           "adamw"};
@@ -121,6 +125,7 @@ struct muon_handle {
     Plan step_plan, ortho_plan;
     AdamPlan adam_plan;
     bool profile = false;
+    uint32_t role_mask = 0;   // roles timed on a profiling handle
     std::vector<Pending> pending;
     std::vector<hipEvent_t> ev_pool;
     int64_t launches[K_NROLES] = {};
@@ -480,7 +485,7 @@ hipEvent_t get_event(muon_handle* h) {
 // records ev0 / ev1 at its start and end.
 template <class F>
 hipError_t timed(muon_handle* h, int role, F&& launch) {
-    if (!h->profile) return launch(nullptr, nullptr);
+    if (!h->profile || !((h->role_mask >> role) & 1u)) return launch(nullptr, nullptr);
     hipEvent_t a = get_event(h), b = get_event(h);
     if (!a || !b) return launch(nullptr, nullptr);
     const hipError_t e = launch(a, b);
@@ -614,7 +619,7 @@ int muon_abi_version(void) { return MUON_ABI_VERSION; }
 muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
     if (!out) return MUON_ERR_INVALID_ARG;
     *out = nullptr;
-    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC)) return MUON_ERR_INVALID_ARG;
+    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC | MUON_INIT_PROFILE_ROLES(0x1FFu))) return MUON_ERR_INVALID_ARG;
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
         (void)hipGetLastError();
@@ -626,6 +631,8 @@ muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
     h->device = device;
     h->flags = flags;
     h->profile = (flags & MUON_INIT_PROFILE) != 0;
+    h->role_mask = (flags >> 16) & 0x1FFu;
+    if (h->role_mask == 0) h->role_mask = (1u << K_NROLES) - 1u;
     *out = h;
     return MUON_OK;
 }

@@ -138,3 +138,11 @@ def test_adamw_hparams_marshalling():
     c = nsm.AdamWHparams(lr=0.25, beta1=0.5, beta2=0.75, eps=1e-6, weight_decay=0.125, step=7).to_c()
     assert (c.lr, c.beta1, c.beta2, c.weight_decay, c.step) == (0.25, 0.5, 0.75, 0.125, 7)
     assert c.eps == pytest.approx(1e-6, rel=1e-7)
+
+
+def test_profile_role_flags(lib):
+    assert nsm.profile_roles(["ns_axpy"]) == 1 << (16 + 4)
+    assert nsm.profile_roles(["momentum_norm", "adamw"]) == (1 | 1 << 8) << 16
+    h = ctypes.c_void_p()
+    # role bits beyond the last role are unknown flag bits: rejected before any device query
+    assert lib.muon_init(ctypes.byref(h), 0, nsm.MUON_INIT_PROFILE | (1 << (16 + 9))) == nsm.MUON_ERR_INVALID_ARG

@@ -410,3 +410,72 @@ def test_forced_allocation_failure():
         assert nsm.muon_workspace_bytes(h) == 0
     finally:
         nsm.muon_destroy(h)
+
+
+def test_step_captured_in_a_hip_graph():
+    """After one eager call (plan built, descriptor table resident), a step
+    with the same pointers enqueues kernels only, so it can be captured into
+    a HIP graph.  Replays with fresh gradients copied into the captured
+    buffers, with eager work and synchronisation between them, match an eager
+    twin bit for bit at every step."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    from muon_synth import make_grad, make_param, encode_storage
+    wl = _wl("graph", [(300, 100), (128, 384), (96, 96)], steps=5, nesterov=True, weight_decay=0.01)
+    n = len(wl.mats)
+    hp = nsm.Hparams(lr=wl.lr, weight_decay=wl.weight_decay, nesterov=True)
+    grads = {s: [to_device(encode_storage(make_grad(wl, s, i), "bf16")) for i in range(n)] for s in range(1, 6)}
+    w0 = [to_device(encode_storage(make_param(wl, i), "bf16")) for i in range(n)]
+    h_g, h_e = nsm.muon_init(0), nsm.muon_init(0)
+    try:
+        # graph side: static buffers
+        w_g = [w.clone() for w in w0]
+        m_g = [torch.zeros(s.rows, s.cols, device="cuda") for s in wl.mats]
+        g_g = [g.clone() for g in grads[1]]
+        # eager twin
+        w_e = [w.clone() for w in w0]
+        m_e = [torch.zeros(s.rows, s.cols, device="cuda") for s in wl.mats]
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            nsm.muon_step(h_g, w_g, g_g, m_g, hp)          # step 1, eager: builds the plan
+        torch.cuda.current_stream().wait_stream(stream)
+        nsm.muon_step(h_e, w_e, grads[1], m_e, hp)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            nsm.muon_step(h_g, w_g, g_g, m_g, hp)
+        torch.cuda.synchronize()
+        for s in range(2, 6):
+            for i in range(n):
+                g_g[i].copy_(grads[s][i])
+            graph.replay()
+            nsm.muon_step(h_e, w_e, grads[s], m_e, hp)
+            junk = torch.randn(1000, device="cuda").sum()   # unrelated eager work between replays
+            torch.cuda.synchronize()
+            assert torch.isfinite(junk)
+            for i in range(n):
+                assert torch.equal(w_g[i], w_e[i]), f"replay {s}: weights of matrix {i} differ"
+                assert torch.equal(m_g[i], m_e[i]), f"replay {s}: momentum of matrix {i} differs"
+    finally:
+        nsm.muon_destroy(h_g)
+        nsm.muon_destroy(h_e)
+
+
+def test_profiling_limited_to_chosen_roles():
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    g = torch.randn(128, 256, device="cuda")
+    for roles, expect in ((["ns_axpy"], {"ns_axpy"}), ([], {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
+                                                             "ns_axpy", "ns_axpy_update"})):
+        h = nsm.muon_init(0, nsm.MUON_INIT_PROFILE | nsm.profile_roles(roles))
+        try:
+            w, m = torch.zeros_like(g), torch.zeros_like(g)
+            nsm.muon_step(h, [w], [g], [m], nsm.Hparams())
+            torch.cuda.synchronize()
+            st = nsm.muon_kernel_stats_read(h)
+            assert set(st) == expect, st
+            if roles == ["ns_axpy"]:
+                assert st["ns_axpy"][0] == 4     # iterations 1-4; the last one is ns_axpy_update
+        finally:
+            nsm.muon_destroy(h)
