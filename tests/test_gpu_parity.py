@@ -66,9 +66,9 @@ def test_gpt2_124m_hidden_workload_sampled():
     print("gpt2-124m worst O rel err", max(e for (_, _, _, e) in rep), "worst mom", max(e for (_, _, e, _) in rep))
 
 
-@pytest.mark.parametrize("ns_steps", [0, 1, 2])
-def test_ns_step_counts(ns_steps):
-    wl = _wl("steps", [(96, 160), (160, 96)], ns_steps=ns_steps, steps=2)
+@pytest.mark.parametrize("ns_steps,nesterov", [(0, False), (1, False), (2, False), (0, True), (1, True)])
+def test_ns_step_counts(ns_steps, nesterov):
+    wl = _wl("steps", [(96, 160), (160, 96)], ns_steps=ns_steps, steps=2, nesterov=nesterov, weight_decay=0.02)
     rec = run_gpu(wl, 2, [0, 1])
     check_against_oracle(wl, rec, TOL_O_BF16)
 
@@ -479,3 +479,17 @@ def test_profiling_limited_to_chosen_roles():
                 assert st["ns_axpy"][0] == 4     # iterations 1-4; the last one is ns_axpy_update
         finally:
             nsm.muon_destroy(h)
+
+
+
+def test_thousands_of_tiny_matrices():
+    """3000 matrices of 1..48 rows and columns in one grouped call (most of
+    them far smaller than one tile), sampled against the oracle."""
+    rng = np.random.default_rng(31)
+    shapes = [(int(rng.integers(1, 49)), int(rng.integers(1, 49))) for _ in range(3000)]
+    wl = _wl("tiny", shapes, steps=2, nesterov=True)
+    check = [0, 1, 2, 999, 1500, 2998, 2999] + [i for i, (r, c) in enumerate(shapes) if r == 1 or c == 1][:3]
+    rep = []
+    rec = run_gpu(wl, 2, check)
+    check_against_oracle(wl, rec, TOL_O_BF16, report=rep)
+    print("tiny worst O rel err", max(e for (_, _, _, e) in rep))
