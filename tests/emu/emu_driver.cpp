@@ -1,9 +1,11 @@
 // Test infrastructure: runs muon_step and muon_adamw_step of the library, built
 // against the CPU stand-in of HIP (tests/emu/hip), on exactly sized host
 // buffers, so AddressSanitizer reports any access outside a caller buffer or
-// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS]
+// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT]]]
 //   SHAPES "RxC,RxC,...", DTYPE 0 = bf16, 1 = f32 (also selects fp32 compute),
-//   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks.
+//   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks,
+//   LD_PAD extra elements per row (views into wider buffers), SHIFT elements
+//   by which every buffer starts past its allocation (unaligned bases).
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -23,6 +25,8 @@ int main(int argc, char** argv) {
     const int ns = std::atoi(argv[2]);
     const int dtype = std::atoi(argv[3]);
     const int block_rows = argc > 4 ? std::atoi(argv[4]) : 0;
+    const long pad = argc > 5 ? std::atol(argv[5]) : 0;
+    const long shift = argc > 6 ? std::atol(argv[6]) : 0;
     std::vector<std::pair<long, long>> shapes;
     for (size_t p = 0; p < spec.size();) {
         size_t q = spec.find(',', p);
@@ -33,15 +37,23 @@ int main(int argc, char** argv) {
     }
     const int es = dtype == 0 ? 2 : 4;
     std::vector<muon_matrix> mats;
+    std::vector<void*> blocks_to_free;
+    auto buf = [&](long r, long ld, long c, int bytes) {
+        // exactly sized: the last row ends at its last element
+        char* p = static_cast<char*>(std::calloc((r - 1) * ld + c + shift, bytes));
+        blocks_to_free.push_back(p);
+        return static_cast<void*>(p + shift * bytes);
+    };
     for (auto [r, c] : shapes) {
         muon_matrix m{};
-        m.param = std::calloc(r * c, es);
-        m.grad = std::calloc(r * c, es);
-        m.momentum = static_cast<float*>(std::calloc(r * c, 4));
-        m.update_out = static_cast<float*>(std::calloc(r * c, 4));
+        const long ld = c + pad;
+        m.param = buf(r, ld, c, es);
+        m.grad = buf(r, ld, c, es);
+        m.momentum = static_cast<float*>(buf(r, ld, c, 4));
+        m.update_out = static_cast<float*>(buf(r, ld, c, 4));
         m.rows = r;
         m.cols = c;
-        m.ld_param = m.ld_grad = m.ld_mom = m.ld_update = c;
+        m.ld_param = m.ld_grad = m.ld_mom = m.ld_update = ld;
         m.dtype = dtype;
         if (block_rows > 0 && r % block_rows == 0) m.block_rows = block_rows;
         mats.push_back(m);
@@ -58,10 +70,10 @@ int main(int argc, char** argv) {
     std::vector<muon_adamw_tensor> ts;
     for (long n : sizes) {
         muon_adamw_tensor t{};
-        t.param = std::calloc(n, es);
-        t.grad = std::calloc(n, es);
-        t.exp_avg = static_cast<float*>(std::calloc(n, 4));
-        t.exp_avg_sq = static_cast<float*>(std::calloc(n, 4));
+        t.param = buf(1, n, n, es);
+        t.grad = buf(1, n, n, es);
+        t.exp_avg = static_cast<float*>(buf(1, n, n, 4));
+        t.exp_avg_sq = static_cast<float*>(buf(1, n, n, 4));
         t.numel = n;
         t.dtype = dtype;
         ts.push_back(t);
@@ -70,17 +82,6 @@ int main(int argc, char** argv) {
     const int st2 = muon_adamw_step(h, ts.data(), static_cast<int>(ts.size()), &ah, nullptr);
     std::printf("adamw %d (%s)\n", st2, muon_last_error(h));
     muon_destroy(h);
-    for (auto& m : mats) {
-        std::free(m.param);
-        std::free(const_cast<void*>(m.grad));
-        std::free(m.momentum);
-        std::free(m.update_out);
-    }
-    for (auto& t : ts) {
-        std::free(t.param);
-        std::free(const_cast<void*>(t.grad));
-        std::free(t.exp_avg);
-        std::free(t.exp_avg_sq);
-    }
+    for (void* p : blocks_to_free) std::free(p);
     return st != MUON_OK ? 4 : (st2 != MUON_OK ? 5 : 0);
 }

@@ -17,7 +17,10 @@ EMU = os.path.join(ROOT, "tests", "emu")
 CXX = "/opt/rocm/lib/llvm/bin/clang++"
 
 CASES = [
+    # shapes, ns_steps, dtype (0 bf16, 1 f32), block rows, leading-dimension pad, misaligned start
     ("300x100,100x300,256x256,129x515,515x129,64x64,1x17,17x1,200x199", 3, 0, 0),
+    ("300x100,100x300,129x515,515x129,1x17,17x1,200x199", 2, 0, 0, 5, 1),
+    ("300x100,100x300,129x515,33x64", 2, 1, 0, 8, 3),
     ("300x100,100x300,256x256,129x515,515x129,64x64,1x17,17x1,200x199", 2, 1, 0),
     ("1x1,1x40,40x1,3x5,64x128,128x64", 2, 1, 0),
     ("1024x3584,3584x1024,1024x1024,1x1,17x1", 2, 0, 0),
@@ -47,11 +50,10 @@ def emu_binary(tmp_path_factory):
     return exe
 
 
-@pytest.mark.parametrize("shapes,ns,dtype,block", CASES)
-def test_kernels_stay_in_bounds(emu_binary, shapes, ns, dtype, block):
+@pytest.mark.parametrize("case", CASES)
+def test_kernels_stay_in_bounds(emu_binary, case):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
-    r = subprocess.run([emu_binary, shapes, str(ns), str(dtype), str(block)], capture_output=True, text=True,
-                       env=env, timeout=600)
+    r = subprocess.run([emu_binary, *[str(v) for v in case]], capture_output=True, text=True, env=env, timeout=600)
     assert "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
     assert r.returncode == 0, (r.stdout, r.stderr[-2000:])
     assert "step 0" in r.stdout and "adamw 0" in r.stdout
