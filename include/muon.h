@@ -26,8 +26,10 @@
  *   - Every data pointer is a device pointer on the handle's device, owned by
  *     the caller, and must stay valid until the stream has passed the work.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *     the call returns without synchronising.  A handle owns one workspace:
- *     calls on one handle must be ordered on one stream (or externally).
+ *     the call returns without synchronising (except the first call of a new
+ *     signature, which waits for its plan upload).  The handle's workspaces
+ *     are shared by its calls: calls on one handle must be ordered on one
+ *     stream (or externally).
  *   - Validation happens before anything is enqueued; a call that returns an
  *     error enqueued nothing and changed no caller memory.
  *   - NaN/Inf inputs are not checked; they propagate within their matrix.
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -61,7 +63,10 @@ typedef enum muon_dtype {
 
 typedef enum muon_compute {
     MUON_COMPUTE_BF16 = 0,     /* bf16 MFMA operands, fp32 accumulation; X kept between iterations
-                                  to ~16 bits (bf16 copy + 8-bit remainder), A and B in bf16 */
+                                  to ~16 bits (bf16 copy + 8-bit remainder), A and B in bf16.
+                                  Matrices (or blocks) with min(rows, cols) <= 64 run the iteration
+                                  in fp32 in this mode too: their products cost next to nothing and
+                                  bf16 operands cost them the most accuracy */
     MUON_COMPUTE_FP32 = 1      /* fp32 MFMA operands and storage: validation mode */
 } muon_compute;
 
@@ -79,13 +84,14 @@ typedef enum muon_role {
     MUON_ROLE_AXPY_UPDATE = 5, /* "ns_axpy_update" (last iteration and the weight update) */
     MUON_ROLE_DIRECT = 6,      /* "direct_update" (ns_steps == 0) */
     MUON_ROLE_FILL = 7,        /* "fill_zero" (workspace initialisation) */
-    MUON_ROLE_ADAMW = 8        /* "adamw" */
+    MUON_ROLE_ADAMW = 8,       /* "adamw" */
+    MUON_ROLE_RESCALE = 9      /* "norm_rescale" (operand copy of inputs with an extreme norm) */
 } muon_role;
 
 /* With MUON_INIT_PROFILE, time only the roles whose bits are set in `mask`
  * (bit r = role r); no bits = every role.  Each timed launch carries its own
  * start/stop events, which costs a little time per launch. */
-#define MUON_INIT_PROFILE_ROLES(mask) ((((uint32_t)(mask)) & 0x1FFu) << 16)
+#define MUON_INIT_PROFILE_ROLES(mask) ((((uint32_t)(mask)) & 0x3FFu) << 16)
 
 /* One weight matrix of the list handed to muon_step. */
 typedef struct muon_matrix {
@@ -164,20 +170,42 @@ int muon_abi_version(void);
 muon_status muon_init(muon_handle **out, int device, uint32_t flags);
 
 /* One Muon step over `n_mats` matrices (all steps above), enqueued on `stream`.
- * The first call for a given list of shapes/dtypes/compute mode builds a plan and
- * allocates the workspace (about 7 bytes per weight element in bf16 mode, plus
- * two min(rows,cols)^2 bf16 squares per matrix); later calls with the same
- * signature allocate nothing.
+ *
+ * Plans.  The first call for a given signature (the list of shapes, blocks,
+ * dtypes, update_out presence and compute mode) builds a plan: tile lists,
+ * device tables and a workspace of about 7 bytes per weight element in bf16
+ * mode plus two min(rows,cols)^2 bf16 squares per matrix, zero-filled, then
+ * waits for the stream once.  The handle keeps the plan of every signature it
+ * has seen until muon_destroy (grow only): a later call with a known signature
+ * allocates nothing and never synchronises, whichever signature came between.
+ * Per plan the handle keeps up to 16 device copies of descriptor tables (the
+ * call's pointers); a call whose pointers match a resident table enqueues
+ * kernel launches only, otherwise it first uploads its table (an
+ * asynchronous copy from pinned host memory) over the least recently used one.
+ *
+ * Graph capture.  A call on a stream that is being captured into a HIP graph
+ * must find both its plan and a descriptor table with exactly its pointers
+ * resident, i.e. the same call must have run once outside capture; otherwise
+ * it returns MUON_ERR_INVALID_ARG and enqueues nothing.  The graph then reads
+ * that plan's workspace and that table, which stay allocated and unchanged
+ * until muon_destroy (a captured table is never overwritten; later calls with
+ * other pointers use other tables).  Replays therefore act on the captured
+ * buffers; they share the plan's workspace with eager calls of the same
+ * signature, so replays and such calls must be ordered on one stream like any
+ * two calls on the handle.  Destroying the handle invalidates the graph.
+ *
  * A matrix cut into blocks (block_rows/block_cols) enters the plan as one entry
  * per block, in row-major block order; at most 65536 entries per call.
- * A call with the same list of shapes and the same pointers as the handle's
- * previous call enqueues kernel launches only (no allocation, copy or memset),
- * so it may be captured into a HIP graph and replayed.
+ * Normalisation is safe at any finite scale: the sum of squares runs in
+ * double, and an input whose norm lies outside [2^-30, 2^30] is rescaled by a
+ * power of two before the first products (one extra pass over its operand
+ * copy; role MUON_ROLE_RESCALE, whose launch returns at once otherwise).
  * n_mats == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null handle/mats/hp with
  * n_mats > 0, null param/grad/momentum, rows or cols < 1, ld < cols, param == grad,
  * momentum aliasing param or grad, ns_steps outside 0..64, a == 0 or a non-finite
  * coefficient, also in coeffs, a block size < 0 or not dividing its dimension,
- * more than 65536 entries, reserved != 0, n_mats < 0), MUON_ERR_DTYPE, MUON_ERR_OOM,
+ * more than 65536 entries, reserved != 0, n_mats < 0, a capturing stream without
+ * the resident plan and table described above), MUON_ERR_DTYPE, MUON_ERR_OOM,
  * MUON_ERR_HIP. */
 muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
                       const muon_hparams *hp, void *stream);
@@ -202,17 +230,18 @@ muon_status muon_orthogonalize(muon_handle *h, const void *in, float *out,
  * pages give no formula, so it is the standard AdamW (Loshchilov and Hutter,
  * decoupled weight decay, bias-corrected Adam moments).  One launch covers the
  * whole list.  The first call for a list of sizes/dtypes builds a plan (a few
- * bytes of device tables per 4096 elements); later calls with the same sizes
- * allocate nothing.  n == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null
+ * bytes of device tables per 4096 elements); plans and descriptor tables are
+ * cached and captured exactly as for muon_step.  n == 0 is a no-op.  Errors: MUON_ERR_INVALID_ARG (null
  * handle/tensors/hp with n > 0, a null buffer with numel > 0, numel < 0,
  * buffers of one tensor aliasing each other, beta outside [0, 1), eps <= 0,
- * a non-finite lr/eps/weight_decay, step < 1, reserved != 0, n < 0),
- * MUON_ERR_DTYPE, MUON_ERR_OOM, MUON_ERR_HIP. */
+ * a non-finite lr/eps/weight_decay, step < 1, reserved != 0, n < 0, a capturing
+ * stream without the resident plan and table), MUON_ERR_DTYPE, MUON_ERR_OOM,
+ * MUON_ERR_HIP. */
 muon_status muon_adamw_step(muon_handle *h, const muon_adamw_tensor *tensors, int32_t n,
                             const muon_adamw_hparams *hp, void *stream);
 
 /* Frobenius norms ||u||_F of the orthogonalised inputs of the most recent
- * muon_step, one per plan entry (a blocked matrix has one per block, row-major)
+ * muon_step (as enqueued: read after that step's kernels), one per plan entry (a blocked matrix has one per block, row-major)
  * in list order, copied to host memory `out` (n entries; the call
  * synchronises the stream).  Validation hook. */
 muon_status muon_read_norms(muon_handle *h, float *out, int32_t n, void *stream);
@@ -222,7 +251,8 @@ muon_status muon_read_norms(muon_handle *h, float *out, int32_t n, void *stream)
 int32_t muon_kernel_stats_read(muon_handle *h, muon_kernel_stats *out, int32_t max);
 void muon_kernel_stats_reset(muon_handle *h);
 
-/* Workspace bytes currently held by the handle. */
+/* Workspace bytes currently held by the handle: the sum over the plans of
+ * every signature seen (the plans' small device tables not included). */
 int64_t muon_workspace_bytes(const muon_handle *h);
 
 /* Free the handle and its workspace (waits for the device).  NULL is a no-op. */

@@ -13,8 +13,10 @@ import os
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_mi355x.so")
-ABI_VERSION = 4   # the MUON_ABI_VERSION of the header this binding mirrors
+# the in-tree build; MUON_LIBRARY names another build of the same library to load instead
+LIB_PATH = os.environ.get("MUON_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libmuon_mi355x.so")
+ABI_VERSION = 5   # the MUON_ABI_VERSION of the header this binding mirrors
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1
@@ -33,7 +35,7 @@ MUON_INIT_FAIL_ALLOC = 0x2
 
 # kernel roles (muon_role), named as in muon_kernel_stats
 ROLE_NAMES = ("momentum_norm", "norm_finalize", "ns_gram", "ns_poly", "ns_axpy", "ns_axpy_update",
-              "direct_update", "fill_zero", "adamw")
+              "direct_update", "fill_zero", "adamw", "norm_rescale")
 
 
 def profile_roles(names) -> int:
@@ -42,7 +44,7 @@ def profile_roles(names) -> int:
     mask = 0
     for nm in names:
         mask |= 1 << ROLE_NAMES.index(nm)
-    return (mask & 0x1FF) << 16
+    return (mask & 0x3FF) << 16
 
 EXPORTED_SYMBOLS = (
     "muon_abi_version",
@@ -256,10 +258,39 @@ def muon_init(device: int = 0, flags: int = 0) -> int:
     return h.value
 
 
+def _check_device_tensors(what: str, tensors, device=None):
+    """Every tensor a CUDA (HIP) tensor on one device; returns that device."""
+    for t in tensors:
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{what}: tensors must be on the GPU (got one on {t.device})")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{what}: tensors on {device} and {t.device}")
+    return device
+
+
 def make_matrix(param, grad, momentum, update_out=None, block=(0, 0)) -> muon_matrix:
-    """Describe one weight's tensors (device tensors, unit column stride);
-    ``block`` = (block_rows, block_cols) cuts it into separately orthogonalised
-    blocks (0 = the whole dimension)."""
+    """Describe one weight's tensors (device tensors on one device, unit column
+    stride); ``block`` = (block_rows, block_cols) cuts it into separately
+    orthogonalised blocks (0 = the whole dimension).  The C ABI sees only
+    pointers and sizes, so shapes and dtypes are checked here: grad,
+    momentum and update_out have param's shape, momentum and update_out are
+    float32, param and grad share a dtype."""
+    import torch
+    ts = [param, grad, momentum] + ([update_out] if update_out is not None else [])
+    for t in ts:
+        if t.dim() != 2:
+            raise ValueError("muon_step: param, grad, momentum and update_out must be 2-D")
+    shape = tuple(param.shape)
+    for nm, t in (("grad", grad), ("momentum", momentum), ("update_out", update_out)):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"muon_step: {nm} has shape {tuple(t.shape)}, param {shape}")
+    if momentum.dtype != torch.float32:
+        raise ValueError(f"muon_step: momentum must be float32, got {momentum.dtype}")
+    if update_out is not None and update_out.dtype != torch.float32:
+        raise ValueError(f"muon_step: update_out must be float32, got {update_out.dtype}")
+    _check_device_tensors("muon_step", ts)
     return muon_matrix(
         param.data_ptr(), grad.data_ptr(), momentum.data_ptr(),
         update_out.data_ptr() if update_out is not None else None,
@@ -287,7 +318,7 @@ def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp
 
 
 def make_adamw_tensor(param, grad, exp_avg, exp_avg_sq) -> muon_adamw_tensor:
-    """Describe one AdamW tensor (contiguous device tensors of equal size)."""
+    """Describe one AdamW tensor (contiguous device tensors of equal size, on one device)."""
     for t in (param, grad, exp_avg, exp_avg_sq):
         if not t.is_contiguous():
             raise ValueError("AdamW tensors must be contiguous")
@@ -297,6 +328,7 @@ def make_adamw_tensor(param, grad, exp_avg, exp_avg_sq) -> muon_adamw_tensor:
     import torch
     if exp_avg.dtype != torch.float32 or exp_avg_sq.dtype != torch.float32:
         raise ValueError("exp_avg and exp_avg_sq are float32")
+    _check_device_tensors("muon_adamw_step", (param, grad, exp_avg, exp_avg_sq))
     return muon_adamw_tensor(param.data_ptr(), grad.data_ptr(), exp_avg.data_ptr(), exp_avg_sq.data_ptr(), n,
                              _dtype_code(param) if _dtype_code(param) == _dtype_code(grad) else -1, 0)
 
@@ -325,7 +357,13 @@ def muon_step_raw(handle: int, arr, n: int, hp: muon_hparams, stream_ptr: int) -
 
 
 def muon_orthogonalize(handle: int, inp, out, hp: Hparams, stream=None) -> None:
-    """out (float32, same shape) = Newton-Schulz(inp)."""
+    """out (float32, inp's shape, same device) = Newton-Schulz(inp)."""
+    import torch
+    if inp.dim() != 2 or tuple(out.shape) != tuple(inp.shape):
+        raise ValueError(f"muon_orthogonalize: out has shape {tuple(out.shape)}, input {tuple(inp.shape)} (2-D)")
+    if out.dtype != torch.float32:
+        raise ValueError(f"muon_orthogonalize: out must be float32, got {out.dtype}")
+    _check_device_tensors("muon_orthogonalize", (inp, out))
     c_hp = hp.to_c()
     st = load().muon_orthogonalize(handle, inp.data_ptr(), out.data_ptr(), int(inp.shape[0]), int(inp.shape[1]),
                                    _ld(inp), _ld(out), _dtype_code(inp), ctypes.byref(c_hp), _stream_ptr(stream))

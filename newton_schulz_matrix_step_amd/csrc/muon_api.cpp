@@ -12,6 +12,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <memory>
 #include <string>
 #include <vector>
 
@@ -36,21 +38,39 @@ enum KernelRole {
     K_DIRECT,
     K_FILL,
     K_ADAMW,
+    K_RESCALE,
     K_NROLES
 };
 static_assert(K_MOMENTUM == MUON_ROLE_MOMENTUM && K_GRAM == MUON_ROLE_GRAM && K_AXPY == MUON_ROLE_AXPY &&
-                  K_AXPY_LAST == MUON_ROLE_AXPY_UPDATE && K_ADAMW == MUON_ROLE_ADAMW && K_NROLES == 9,
+                  K_AXPY_LAST == MUON_ROLE_AXPY_UPDATE && K_ADAMW == MUON_ROLE_ADAMW &&
+                  K_RESCALE == MUON_ROLE_RESCALE && K_NROLES == 10,
               "kernel roles follow muon_role");
 const char* const kRoleNames[K_NROLES] = {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
                                           "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero",
-                                          "adamw"};
+                                          "adamw", "norm_rescale"};
+constexpr uint32_t kRoleBits = (1u << K_NROLES) - 1u;
 
 constexpr int kStageSlots = 4;
+constexpr int kMaxTables = 16;     // descriptor tables per plan that a new pointer set may overwrite
 constexpr int kMaxNsSteps = 64;
 constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxEntries = 65536;   // plan entries (matrices or blocks) per muon_step call
-constexpr int kUnitElems = 16384;  // momentum-pass elements per workgroup (target)
+#ifndef MUON_UNIT_ELEMS
+#define MUON_UNIT_ELEMS 16384
+#endif
+constexpr int kUnitElems = MUON_UNIT_ELEMS;  // momentum-pass elements per workgroup (target)
+// 256-wide tiles: bf16-iteration entries with min(R, C) >= kWideMinM are
+// padded to 256 and run the phases in kWidePhases (bit 0 GRAM, 1 POLY, 2 AXPY)
+// on 256 x 256 tiles, the rest on 128 x 128.
+#ifndef MUON_WIDE_MIN_M
+#define MUON_WIDE_MIN_M (1 << 30)
+#endif
+#ifndef MUON_WIDE_PHASES
+#define MUON_WIDE_PHASES 7
+#endif
+constexpr int kWideMinM = MUON_WIDE_MIN_M;
+constexpr int kWidePhases = MUON_WIDE_PHASES;
 // Tile rows per item of the tile lists (see build_list): GRAM / POLY items of
 // 8 rows; an AXPY output of at most 8 tile rows is one item, taller ones go in
 // items of 4 rows (8 measured slower there).
@@ -58,57 +78,66 @@ constexpr int kItemRowsSym = 8;
 constexpr int kItemRowsAxpyWhole = 8;
 constexpr int kItemRowsAxpy = 4;
 
-
-
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-struct Plan {
-    bool valid = false;
-    std::vector<int64_t> key;
-    int n = 0;
-    bool f32c = false;
-    std::vector<MatDesc> geom;     // static part of every descriptor
-    std::vector<MatDesc> uploaded; // last descriptor table sent to the device
-    bool have_uploaded = false;
-    MatDesc* d_desc = nullptr;
-    // tile lists: 8 per-XCD chunks of equal length (n_* = 8 x chunk), padded
-    // with skip entries (mat = -1)
-    Tile* d_gram = nullptr;
-    int n_gram = 0;
-    int gram_tile = 0;
-    Tile* d_poly = nullptr;
-    int n_poly = 0;
-    Tile* d_axpy = nullptr;
-    int n_axpy = 0;
-    int axpy_tile = 0;
-    Unit* d_units = nullptr;
-    int n_units = 0;
-    float* d_partials = nullptr;
-    float* d_inv = nullptr;
-    float* d_nu = nullptr;
-    char* ws = nullptr;
-    size_t ws_bytes = 0;
-    MatDesc* h_stage[kStageSlots] = {};
-    hipEvent_t stage_ev[kStageSlots] = {};
-    bool stage_used[kStageSlots] = {};
+// Pinned host slots for descriptor uploads: a slot is reused once the copy out
+// of it has completed (its event).
+struct Staging {
+    void* h[kStageSlots] = {};
+    hipEvent_t ev[kStageSlots] = {};
+    bool used[kStageSlots] = {};
     int slot = 0;
+    size_t bytes = 0;
 };
 
-// AdamW: chunk table (static per list of sizes and dtypes) and the last
-// descriptor table sent to the device.
-struct AdamPlan {
-    bool valid = false;
+// One descriptor table on the device: the pointers (and geometry) of one call.
+// A table read by a step captured into a HIP graph is frozen: it is never
+// rewritten, so the graph's replays keep reading exactly what was captured.
+template <class D>
+struct DescTable {
+    D* d = nullptr;
+    std::vector<D> host;       // what the device copy holds
+    bool frozen = false;
+    uint64_t last_use = 0;
+};
+
+template <class D>
+struct TableSet {
+    std::vector<DescTable<D>> tables;
+    Staging stage;
+    uint64_t clock = 0;
+};
+
+struct TileList {
+    Tile* d = nullptr;
+    int n = 0;                 // 8 per-XCD chunks of equal length, padded with mat = -1
+};
+
+// Everything one call signature (list of shapes, dtypes, buffer presence and
+// compute mode) needs, built on first sight and kept until muon_destroy.
+struct Plan {
     std::vector<int64_t> key;
     int n = 0;
-    AdamDesc* d_desc = nullptr;
+    std::vector<MatDesc> geom;     // static part of every descriptor
+    // per phase, one list per kernel: [0] bf16 entries on 128 x 128 tiles,
+    // [1] float32 entries (128 x 128), [2] bf16 entries on 256 x 256 tiles
+    TileList gram[3], poly[3], axpy[3];
+    Unit* d_units = nullptr;
+    int n_units = 0;
+    double* d_partials = nullptr;
+    NormScale* d_norm = nullptr;
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    TableSet<MatDesc> tabs;
+};
+
+// AdamW: chunk table (static per list of sizes and dtypes) and its descriptor tables.
+struct AdamPlan {
+    std::vector<int64_t> key;
+    int n = 0;
     AdamChunk* d_chunks = nullptr;
     int n_chunks = 0;
-    std::vector<AdamDesc> uploaded;
-    bool have_uploaded = false;
-    AdamDesc* h_stage[kStageSlots] = {};
-    hipEvent_t stage_ev[kStageSlots] = {};
-    bool stage_used[kStageSlots] = {};
-    int slot = 0;
+    TableSet<AdamDesc> tabs;
 };
 
 struct Pending {
@@ -122,8 +151,10 @@ struct muon_handle {
     int device = 0;
     uint32_t flags = 0;
     std::string err;
-    Plan step_plan, ortho_plan;
-    AdamPlan adam_plan;
+    std::map<std::vector<int64_t>, std::unique_ptr<Plan>> plans;
+    std::map<std::vector<int64_t>, std::unique_ptr<AdamPlan>> adam_plans;
+    Plan* last_step = nullptr;   // plan of the latest muon_step (norm readback)
+    int last_step_n = 0;
     bool profile = false;
     uint32_t role_mask = 0;   // roles timed on a profiling handle
     std::vector<Pending> pending;
@@ -163,31 +194,120 @@ struct DeviceGuard {
     }
 };
 
-void free_adam_plan(AdamPlan& p) {
-    (void)hipFree(p.d_desc);
-    (void)hipFree(p.d_chunks);
+void free_staging(Staging& st) {
     for (int i = 0; i < kStageSlots; ++i) {
-        if (p.stage_ev[i]) (void)hipEventDestroy(p.stage_ev[i]);
-        if (p.h_stage[i]) (void)hipHostFree(p.h_stage[i]);
+        if (st.ev[i]) (void)hipEventDestroy(st.ev[i]);
+        if (st.h[i]) (void)hipHostFree(st.h[i]);
     }
-    p = AdamPlan();
+    st = Staging();
+}
+
+template <class D>
+void free_tables(TableSet<D>& ts) {
+    for (DescTable<D>& t : ts.tables) (void)hipFree(t.d);
+    ts.tables.clear();
+    free_staging(ts.stage);
 }
 
 void free_plan(Plan& p) {
-    (void)hipFree(p.d_desc);
-    (void)hipFree(p.d_gram);
-    (void)hipFree(p.d_poly);
-    (void)hipFree(p.d_axpy);
+    for (int m = 0; m < 3; ++m) {
+        (void)hipFree(p.gram[m].d);
+        (void)hipFree(p.poly[m].d);
+        (void)hipFree(p.axpy[m].d);
+    }
     (void)hipFree(p.d_units);
     (void)hipFree(p.d_partials);
-    (void)hipFree(p.d_inv);
-    (void)hipFree(p.d_nu);
+    (void)hipFree(p.d_norm);
     (void)hipFree(p.ws);
-    for (int i = 0; i < kStageSlots; ++i) {
-        if (p.stage_ev[i]) (void)hipEventDestroy(p.stage_ev[i]);
-        if (p.h_stage[i]) (void)hipHostFree(p.h_stage[i]);
-    }
+    free_tables(p.tabs);
     p = Plan();
+}
+
+void free_adam_plan(AdamPlan& p) {
+    (void)hipFree(p.d_chunks);
+    free_tables(p.tabs);
+    p = AdamPlan();
+}
+
+muon_status alloc_staging(muon_handle* h, Staging& st, size_t bytes) {
+    st.bytes = std::max<size_t>(bytes, 16);
+    for (int i = 0; i < kStageSlots; ++i)
+        if (hipHostMalloc(&st.h[i], st.bytes, hipHostMallocDefault) != hipSuccess ||
+            hipEventCreateWithFlags(&st.ev[i], hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(h, MUON_ERR_OOM, "descriptor staging allocation failed");
+        }
+    return MUON_OK;
+}
+
+// Is `stream` being captured into a graph?  A capturing call may only enqueue
+// kernels that read state already on the device.
+muon_status capture_state(muon_handle* h, hipStream_t stream, bool* capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(h, e, "hipStreamIsCapturing");
+    }
+    *capturing = cs != hipStreamCaptureStatusNone;
+    return MUON_OK;
+}
+
+// The device descriptor table holding exactly `desc`: an existing table when
+// one matches (no upload), else an upload into the least recently used table
+// that no captured graph reads (a new table while fewer than kMaxTables are
+// in use).  Under capture only an existing table may serve, and it is frozen.
+template <class D>
+muon_status select_table(muon_handle* h, TableSet<D>& ts, const std::vector<D>& desc, bool capturing,
+                         hipStream_t stream, const D** out) {
+    const size_t bytes = sizeof(D) * desc.size();
+    ++ts.clock;
+    for (DescTable<D>& t : ts.tables)
+        if (t.host.size() == desc.size() && std::memcmp(t.host.data(), desc.data(), bytes) == 0) {
+            if (capturing) t.frozen = true;
+            t.last_use = ts.clock;
+            *out = t.d;
+            return MUON_OK;
+        }
+    if (capturing)
+        return fail(h, MUON_ERR_INVALID_ARG,
+                    "a call captured into a HIP graph must first run once outside capture with the same shapes "
+                    "and pointers (its plan and descriptor table are then resident)");
+    DescTable<D>* slot = nullptr;
+    int free_tables_n = 0;
+    for (DescTable<D>& t : ts.tables)
+        if (!t.frozen) {
+            ++free_tables_n;
+            if (!slot || t.last_use < slot->last_use) slot = &t;
+        }
+    if (!slot || free_tables_n < kMaxTables) {
+        if (h->flags & MUON_INIT_FAIL_ALLOC)
+            return fail(h, MUON_ERR_OOM, "descriptor table allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
+        DescTable<D> t;
+        if (hipMalloc(reinterpret_cast<void**>(&t.d), std::max<size_t>(bytes, 16)) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(h, MUON_ERR_OOM, "descriptor table allocation failed");
+        }
+        ts.tables.push_back(std::move(t));
+        slot = &ts.tables.back();
+    }
+    Staging& st = ts.stage;
+    const int s = st.slot;
+    hipError_t e;
+    if (st.used[s]) {
+        e = hipEventSynchronize(st.ev[s]);
+        if (e != hipSuccess) return hip_fail(h, e, "descriptor staging wait");
+    }
+    std::memcpy(st.h[s], desc.data(), bytes);
+    e = hipMemcpyAsync(slot->d, st.h[s], bytes, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipEventRecord(st.ev[s], stream);
+    if (e != hipSuccess) return hip_fail(h, e, "descriptor upload");
+    st.used[s] = true;
+    st.slot = (s + 1) % kStageSlots;
+    slot->host = desc;
+    slot->last_use = ts.clock;
+    *out = slot->d;
+    return MUON_OK;
 }
 
 // Everything a caller passes for one matrix, before validation.
@@ -277,24 +397,18 @@ muon_status append_blocks(muon_handle* h, const MatIn& m, int32_t block_rows, in
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Static geometry, workspace layout, units and tiles for one call signature.
-muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, bool f32c,
-                       const std::vector<int64_t>& key, hipStream_t stream) {
-    if (p.valid || p.ws) {
-        hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize before re-plan");
-        free_plan(p);
-    }
+muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, const std::vector<int64_t>& key,
+                       hipStream_t stream, Plan** out) {
     const int n = int(mats.size());
-    const int64_t es = f32c ? 4 : 2;
     std::vector<MatDesc> geom(n);
     std::vector<Unit> units;
-    std::vector<Tile> gram, axpy;
     size_t off = 0;
     auto take = [&](int64_t bytes) {
         const size_t o = off;
         off += size_t(round_up(bytes, 256));
         return int64_t(o);
     };
+    std::vector<char> wide(n, 0);   // entry padded to 256 (some phases on 256 x 256 tiles)
     for (int i = 0; i < n; ++i) {
         const MatIn& m = mats[i];
         MatDesc d;
@@ -304,17 +418,21 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         d.trans = m.R > m.C;
         d.m = int32_t(std::min(m.R, m.C));
         d.n = int32_t(std::max(m.R, m.C));
-        d.Rp = int32_t(round_up(m.R, kPad));
-        d.Cp = int32_t(round_up(m.C, kPad));
-        d.mp = int32_t(round_up(d.m, kPad));
-        d.np = int32_t(round_up(d.n, kPad));
+        d.f32 = f32c || d.m <= kSmallM;
+        wide[i] = !d.f32 && d.m >= kWideMinM && kWidePhases != 0;
+        const int64_t pad = wide[i] ? 256 : kPad;
+        d.Rp = int32_t(round_up(m.R, pad));
+        d.Cp = int32_t(round_up(m.C, pad));
+        d.mp = int32_t(round_up(d.m, pad));
+        d.np = int32_t(round_up(d.n, pad));
         d.io_dtype = m.dtype;
         d.has_param = m.has_param;
         d.has_mom = m.has_mom;
         d.shape_scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));
+        const int64_t es = d.f32 ? 4 : 2;
         const int64_t xe = int64_t(d.mp) * d.np;
         d.off_u = take(int64_t(d.Rp) * d.Cp * es);
-        d.off_xlo = f32c ? 0 : take(xe);
+        d.off_xlo = d.f32 ? 0 : take(xe);
         d.off_xb0 = take(xe * es);
         d.off_xb1 = take(xe * es);
         d.off_a = take(int64_t(d.mp) * d.mp * es);
@@ -327,29 +445,33 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         d.nunits = int32_t(units.size()) - d.unit0;
         geom[i] = d;
     }
-
-    // Newton-Schulz tile edge: 128 x 128 in bf16 mode for every phase.  Two
-    // workgroups share a CU, so one tile's epilogue overlaps another's main
-    // loop; AXPY tiles of this size also keep their quadrant of X from the
-    // operand stream.  256-wide tiles (one workgroup per CU, half the operand
-    // traffic per flop) measured slower on every workload once those
-    // epilogue savings were in.
-    const int gram_tile = f32c ? kTileF32 : kTileBf16;
-    const int axpy_tile = gram_tile;
-    // Tile lists.  Workgroup b runs on XCD b % 8, and each XCD has its own L2,
-    // so every list is 8 chunks, one per XCD: chunk x holds the tiles XCD x
-    // runs, in dispatch order.  Tiles come in items (one matrix's group of up
-    // to 4 or 8 tile rows across all tile columns, which share operand panels;
-    // within an item the rows of one column are consecutive);
-    // items are dealt to the XCDs largest first, each to the least-loaded one
-    // (load = tiles x k blocks), so every XCD gets about the same work however
-    // mixed the matrix shapes (keeping a matrix on one XCD for L2 reuse
-    // measured slower: it costs balance); within a chunk, the longest-k tiles
-    // go first.
-    // GRAM (k = n) and POLY (k = m) weigh the same tiles differently, so each
-    // gets its own list.
-    auto build_list = [&](int T, int kind, std::vector<Tile>& out) {
+    // Newton-Schulz tile edges: 128 x 128 (two workgroups share a CU, so one
+    // tile's epilogue overlaps another's main loop; AXPY tiles of this size
+    // keep their quadrant of X from the operand stream) and, for the entries
+    // and phases the wide-tile policy above selects, 256 x 256 (one workgroup
+    // per CU, half the operand traffic and half the LDS reads per flop).
+    static_assert(kTileBf16 == kTileF32 && kTileBf16 == 128, "128 x 128 base tiles in both modes");
+    // list kind of entry i in a phase: 0 bf16 on 128 tiles, 1 float32, 2 bf16 on 256 tiles
+    auto list_kind = [&](int i, int kind) {
+        if (geom[i].f32) return 1;
+        const int bit = kind == PH_GRAM ? 1 : (kind == PH_POLY ? 2 : 4);
+        return (wide[i] && (kWidePhases & bit)) ? 2 : 0;
+    };
+    // Tile lists, one per phase and per kernel (bf16 128 / float32 / bf16 256
+    // entries run different kernels).  Workgroup b runs on XCD b % 8, and each
+    // XCD has its own L2, so every list is 8 chunks, one per XCD: chunk x
+    // holds the tiles XCD x runs, in dispatch order.  Tiles come in items (one
+    // matrix's group of up to 4 or 8 tile rows across all tile columns, which
+    // share operand panels; within an item the rows of one column are
+    // consecutive); items are dealt to the XCDs largest first, each to the
+    // least-loaded one (load = tiles x k blocks), so every XCD gets about the
+    // same work however mixed the matrix shapes (keeping a matrix on one XCD
+    // for L2 reuse measured slower: it costs balance); within a chunk, the
+    // longest-k tiles go first.  GRAM (k = n) and POLY (k = m) weigh the same
+    // tiles differently, so each gets its own list.
+    auto build_list = [&](int kind, int lk, std::vector<Tile>& out) {
         const bool sym = kind != PH_AXPY;
+        const int T = lk == 2 ? 256 : 128;
         struct Item {
             int mat, a0;
             int64_t w;
@@ -366,6 +488,7 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         };
         auto item_rows = [&](int tm) { return sym ? kItemRowsSym : (tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy); };
         for (int i = 0; i < n; ++i) {
+            if (list_kind(i, kind) != lk) continue;
             int tm, tn;
             dims(geom[i], tm, tn);
             const int IR = item_rows(tm);
@@ -375,6 +498,8 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
                 items.push_back(Item{i, a0, cnt * ksteps(geom[i])});
             }
         }
+        out.clear();
+        if (items.empty()) return;
         std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.w > y.w; });
         std::vector<Tile> bins[8];
         int64_t load[8] = {};
@@ -400,73 +525,80 @@ muon_status build_plan(muon_handle* h, Plan& p, const std::vector<MatIn>& mats, 
         out.assign(8 * chunk, Tile{-1, 0, 0, 0});
         for (int x = 0; x < 8; ++x) std::copy(bins[x].begin(), bins[x].end(), out.begin() + x * chunk);
     };
-    std::vector<Tile> poly;
-    build_list(gram_tile, PH_GRAM, gram);
-    build_list(gram_tile, PH_POLY, poly);
-    build_list(axpy_tile, PH_AXPY, axpy);
+    std::vector<Tile> lists[3][3];
+    for (int lk = 0; lk < 3; ++lk) {
+        build_list(PH_GRAM, lk, lists[0][lk]);
+        build_list(PH_POLY, lk, lists[1][lk]);
+        build_list(PH_AXPY, lk, lists[2][lk]);
+    }
     // every tile's operand panels must lie inside the padded workspace buffers
-    for (const std::vector<Tile>* lst : {&gram, &poly})
-        for (const Tile& t : *lst) {
+    for (int lk = 0; lk < 3; ++lk) {
+        const int T = lk == 2 ? 256 : 128;
+        for (int l = 0; l < 2; ++l)
+            for (const Tile& t : lists[l][lk]) {
+                if (t.mat < 0) continue;
+                const MatDesc& d = geom[t.mat];
+                if ((t.ti + 1) * T > d.mp || (t.tj + 1) * T > d.mp || t.tj < t.ti)
+                    return fail(h, MUON_ERR_HIP, "internal: gram tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
+            }
+        for (const Tile& t : lists[2][lk]) {
             if (t.mat < 0) continue;
             const MatDesc& d = geom[t.mat];
-            if ((t.ti + 1) * gram_tile > d.mp || (t.tj + 1) * gram_tile > d.mp || t.tj < t.ti)
-                return fail(h, MUON_ERR_HIP, "internal: gram tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
+            if ((t.ti + 1) * T > d.Rp || (t.tj + 1) * T > d.Cp)
+                return fail(h, MUON_ERR_HIP, "internal: axpy tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
         }
-    for (const Tile& t : axpy) {
-        if (t.mat < 0) continue;
-        const MatDesc& d = geom[t.mat];
-        if ((t.ti + 1) * axpy_tile > d.Rp || (t.tj + 1) * axpy_tile > d.Cp)
-            return fail(h, MUON_ERR_HIP, "internal: axpy tile (%d, %d) outside matrix %d", t.ti, t.tj, t.mat);
     }
 
     if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "workspace allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
 
-    Plan q;
+    std::unique_ptr<Plan> q(new (std::nothrow) Plan());
+    if (!q) return fail(h, MUON_ERR_OOM, "plan allocation failed");
     auto dmalloc = [&](void** ptr, size_t bytes) -> bool {
         return hipMalloc(ptr, std::max<size_t>(bytes, 16)) == hipSuccess;
     };
-    bool ok = dmalloc(reinterpret_cast<void**>(&q.d_desc), sizeof(MatDesc) * n) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_gram), sizeof(Tile) * gram.size()) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_poly), sizeof(Tile) * poly.size()) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_axpy), sizeof(Tile) * axpy.size()) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_units), sizeof(Unit) * units.size()) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_partials), sizeof(float) * units.size()) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_inv), sizeof(float) * n) &&
-              dmalloc(reinterpret_cast<void**>(&q.d_nu), sizeof(float) * n) &&
-              dmalloc(reinterpret_cast<void**>(&q.ws), off);
-    for (int i = 0; ok && i < kStageSlots; ++i) {
-        ok = hipHostMalloc(reinterpret_cast<void**>(&q.h_stage[i]), sizeof(MatDesc) * std::max(n, 1), hipHostMallocDefault) == hipSuccess &&
-             hipEventCreateWithFlags(&q.stage_ev[i], hipEventDisableTiming) == hipSuccess;
-    }
+    TileList* tl[3] = {q->gram, q->poly, q->axpy};
+    bool ok = true;
+    for (int l = 0; ok && l < 3; ++l)
+        for (int lk = 0; ok && lk < 3; ++lk)
+            if (!lists[l][lk].empty())
+                ok = dmalloc(reinterpret_cast<void**>(&tl[l][lk].d), sizeof(Tile) * lists[l][lk].size());
+    ok = ok && dmalloc(reinterpret_cast<void**>(&q->d_units), sizeof(Unit) * units.size()) &&
+         dmalloc(reinterpret_cast<void**>(&q->d_partials), sizeof(double) * units.size()) &&
+         dmalloc(reinterpret_cast<void**>(&q->d_norm), sizeof(NormScale) * n) &&
+         dmalloc(reinterpret_cast<void**>(&q->ws), off);
     if (!ok) {
         (void)hipGetLastError();
-        free_plan(q);
+        free_plan(*q);
         return fail(h, MUON_ERR_OOM, "workspace allocation of %.3f GB failed", double(off) / 1e9);
     }
-    q.ws_bytes = off;
-    hipError_t e = launch_fill_zero(q.ws, off, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(q.d_gram, gram.data(), sizeof(Tile) * gram.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(q.d_poly, poly.data(), sizeof(Tile) * poly.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(q.d_axpy, axpy.data(), sizeof(Tile) * axpy.size(), hipMemcpyHostToDevice, stream);
-    if (e == hipSuccess) e = hipMemcpyAsync(q.d_units, units.data(), sizeof(Unit) * units.size(), hipMemcpyHostToDevice, stream);
+    muon_status st = alloc_staging(h, q->tabs.stage, sizeof(MatDesc) * n);
+    if (st != MUON_OK) {
+        free_plan(*q);
+        return st;
+    }
+    q->ws_bytes = off;
+    hipError_t e = launch_fill_zero(q->ws, off, stream);
+    for (int l = 0; e == hipSuccess && l < 3; ++l)
+        for (int lk = 0; e == hipSuccess && lk < 3; ++lk)
+            if (!lists[l][lk].empty()) {
+                e = hipMemcpyAsync(tl[l][lk].d, lists[l][lk].data(), sizeof(Tile) * lists[l][lk].size(),
+                                   hipMemcpyHostToDevice, stream);
+                tl[l][lk].n = int(lists[l][lk].size());
+            }
+    if (e == hipSuccess) e = hipMemcpyAsync(q->d_units, units.data(), sizeof(Unit) * units.size(), hipMemcpyHostToDevice, stream);
     // the host vectors die with this call: wait for the copies
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
-        free_plan(q);
+        free_plan(*q);
         return hip_fail(h, e, "plan upload");
     }
-    q.n = n;
-    q.f32c = f32c;
-    q.geom = std::move(geom);
-    q.n_gram = int(gram.size());
-    q.n_poly = int(poly.size());
-    q.n_axpy = int(axpy.size());
-    q.gram_tile = gram_tile;
-    q.axpy_tile = axpy_tile;
-    q.n_units = int(units.size());
-    q.key = key;
-    q.valid = true;
-    p = std::move(q);
+    q->n = n;
+    q->geom = std::move(geom);
+    q->n_units = int(units.size());
+    q->key = key;
+    Plan* raw = q.get();
+    h->plans[key] = std::move(q);
+    *out = raw;
     return MUON_OK;
 }
 
@@ -493,9 +625,33 @@ hipError_t timed(muon_handle* h, int role, F&& launch) {
     return e;
 }
 
-muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream) {
+// One phase over its tile lists (bf16 entries on 128 tiles, float32 entries,
+// bf16 entries on 256 tiles); on a profiling handle the phase is timed as one,
+// from the first launch's start to the last one's end.
+hipError_t launch_phase_lists(int kind, const TileList (&l)[3], const MatDesc* desc, const PhaseArgs& pa,
+                              hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+    int first = -1, last = -1;
+    for (int lk = 0; lk < 3; ++lk)
+        if (l[lk].n) {
+            if (first < 0) first = lk;
+            last = lk;
+        }
+    for (int lk = 0; lk < 3; ++lk) {
+        if (!l[lk].n) continue;
+        const hipError_t e = launch_ns_phase(kind, lk == 1, lk == 2 ? 256 : 128, l[lk].d, l[lk].n, desc, pa, stream,
+                                             lk == first ? e0 : nullptr, lk == last ? e1 : nullptr);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream,
+                 Plan** used) {
     const int n = int(mats.size());
     const bool f32c = hp->compute == MUON_COMPUTE_FP32;
+    bool capturing = false;
+    muon_status st = capture_state(h, stream, &capturing);
+    if (st != MUON_OK) return st;
     std::vector<int64_t> key;
     key.reserve(2 + 5 * size_t(n));
     key.push_back(n);
@@ -507,10 +663,19 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
         key.push_back(m.has_param);
         key.push_back(m.has_mom);
     }
-    if (!plan.valid || plan.key != key) {
-        muon_status st = build_plan(h, plan, mats, f32c, key, stream);
+    Plan* pp = nullptr;
+    auto it = h->plans.find(key);
+    if (it != h->plans.end()) {
+        pp = it->second.get();
+    } else {
+        if (capturing)
+            return fail(h, MUON_ERR_INVALID_ARG,
+                        "a call captured into a HIP graph must first run once outside capture with the same shapes "
+                        "and pointers (its plan and descriptor table are then resident)");
+        st = build_plan(h, mats, f32c, key, stream, &pp);
         if (st != MUON_OK) return st;
     }
+    Plan& plan = *pp;
 
     // descriptor table: static geometry + this call's pointers
     std::vector<MatDesc> desc(plan.geom);
@@ -536,40 +701,28 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
                        (!m.upd || ((m.ld_upd % 4 == 0) && al(m.upd, 16)));
         }
     }
-    hipError_t e;
-    if (!plan.have_uploaded || std::memcmp(desc.data(), plan.uploaded.data(), sizeof(MatDesc) * n) != 0) {
-        const int s = plan.slot;
-        if (plan.stage_used[s]) {
-            e = hipEventSynchronize(plan.stage_ev[s]);
-            if (e != hipSuccess) return hip_fail(h, e, "descriptor staging wait");
-        }
-        std::memcpy(plan.h_stage[s], desc.data(), sizeof(MatDesc) * n);
-        e = hipMemcpyAsync(plan.d_desc, plan.h_stage[s], sizeof(MatDesc) * n, hipMemcpyHostToDevice, stream);
-        if (e == hipSuccess) e = hipEventRecord(plan.stage_ev[s], stream);
-        if (e != hipSuccess) return hip_fail(h, e, "descriptor upload");
-        plan.stage_used[s] = true;
-        plan.slot = (s + 1) % kStageSlots;
-        plan.uploaded = desc;
-        plan.have_uploaded = true;
-    }
+    const MatDesc* d_desc = nullptr;
+    st = select_table(h, plan.tabs, desc, capturing, stream, &d_desc);
+    if (st != MUON_OK) return st;
+    if (used) *used = pp;
 
     MomentumArgs ma;
     ma.ws = plan.ws;
     ma.partials = plan.d_partials;
     ma.beta = hp->beta;
     ma.nesterov = hp->nesterov;
-    e = timed(h, K_MOMENTUM, [&](hipEvent_t e0, hipEvent_t e1) {
-        return launch_momentum(plan.d_units, plan.n_units, plan.d_desc, ma, f32c, stream, e0, e1);
+    hipError_t e = timed(h, K_MOMENTUM, [&](hipEvent_t e0, hipEvent_t e1) {
+        return launch_momentum(plan.d_units, plan.n_units, d_desc, ma, stream, e0, e1);
     });
     if (e != hipSuccess) return hip_fail(h, e, "momentum launch");
     e = timed(h, K_FINALIZE, [&](hipEvent_t e0, hipEvent_t e1) {
-        return launch_finalize_norm(plan.d_desc, n, plan.d_partials, plan.d_inv, plan.d_nu, hp->eps, stream, e0, e1);
+        return launch_finalize_norm(d_desc, n, plan.d_partials, plan.d_norm, hp->eps, stream, e0, e1);
     });
     if (e != hipSuccess) return hip_fail(h, e, "norm launch");
 
     PhaseArgs pa;
     pa.ws = plan.ws;
-    pa.inv_norm = plan.d_inv;
+    pa.norm = plan.d_norm;
     pa.a = hp->a;
     pa.b = hp->b;
     pa.c = hp->c;
@@ -580,11 +733,15 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
     pa.iter = 0;
     if (hp->ns_steps == 0) {
         e = timed(h, K_DIRECT, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_direct_update(plan.d_units, plan.n_units, plan.d_desc, pa, stream, e0, e1);
+            return launch_direct_update(plan.d_units, plan.n_units, d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "update launch");
         return MUON_OK;
     }
+    e = timed(h, K_RESCALE, [&](hipEvent_t e0, hipEvent_t e1) {
+        return launch_rescale(plan.d_units, plan.n_units, d_desc, plan.d_norm, plan.ws, stream, e0, e1);
+    });
+    if (e != hipSuccess) return hip_fail(h, e, "rescale launch");
     for (int it = 1; it <= hp->ns_steps; ++it) {
         pa.iter = it;
         if (hp->coeffs) {   // this iteration's triple
@@ -593,17 +750,16 @@ muon_status run(muon_handle* h, Plan& plan, const std::vector<MatIn>& mats, cons
             pa.c = hp->coeffs[3 * (it - 1) + 2];
         }
         e = timed(h, K_GRAM, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_ns_phase(PH_GRAM, f32c, plan.gram_tile, plan.d_gram, plan.n_gram, plan.d_desc, pa, stream, e0, e1);
+            return launch_phase_lists(PH_GRAM, plan.gram, d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "gram launch");
         e = timed(h, K_POLY, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_ns_phase(PH_POLY, f32c, plan.gram_tile, plan.d_poly, plan.n_poly, plan.d_desc, pa, stream, e0, e1);
+            return launch_phase_lists(PH_POLY, plan.poly, d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "poly launch");
         const bool last = it == hp->ns_steps;
         e = timed(h, last ? K_AXPY_LAST : K_AXPY, [&](hipEvent_t e0, hipEvent_t e1) {
-            return launch_ns_phase(last ? PH_AXPY_LAST : PH_AXPY, f32c, plan.axpy_tile, plan.d_axpy, plan.n_axpy,
-                                   plan.d_desc, pa, stream, e0, e1);
+            return launch_phase_lists(last ? PH_AXPY_LAST : PH_AXPY, plan.axpy, d_desc, pa, stream, e0, e1);
         });
         if (e != hipSuccess) return hip_fail(h, e, "axpy launch");
     }
@@ -619,7 +775,7 @@ int muon_abi_version(void) { return MUON_ABI_VERSION; }
 muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
     if (!out) return MUON_ERR_INVALID_ARG;
     *out = nullptr;
-    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC | MUON_INIT_PROFILE_ROLES(0x1FFu))) return MUON_ERR_INVALID_ARG;
+    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC | MUON_INIT_PROFILE_ROLES(kRoleBits))) return MUON_ERR_INVALID_ARG;
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
         (void)hipGetLastError();
@@ -631,8 +787,8 @@ muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
     h->device = device;
     h->flags = flags;
     h->profile = (flags & MUON_INIT_PROFILE) != 0;
-    h->role_mask = (flags >> 16) & 0x1FFu;
-    if (h->role_mask == 0) h->role_mask = (1u << K_NROLES) - 1u;
+    h->role_mask = (flags >> 16) & kRoleBits;
+    if (h->role_mask == 0) h->role_mask = kRoleBits;
     *out = h;
     return MUON_OK;
 }
@@ -659,7 +815,13 @@ muon_status muon_step(muon_handle* h, const muon_matrix* mats, int32_t n_mats, c
     }
     DeviceGuard g(h->device);
     if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
-    return run(h, h->step_plan, in, hp, static_cast<hipStream_t>(stream));
+    Plan* used = nullptr;
+    st = run(h, in, hp, static_cast<hipStream_t>(stream), &used);
+    if (used) {
+        h->last_step = used;
+        h->last_step_n = int(in.size());
+    }
+    return st;
 }
 
 muon_status muon_orthogonalize(muon_handle* h, const void* in, float* out, int64_t rows, int64_t cols, int64_t ld_in,
@@ -676,49 +838,45 @@ muon_status muon_orthogonalize(muon_handle* h, const void* in, float* out, int64
     if (st != MUON_OK) return st;
     DeviceGuard g(h->device);
     if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
-    return run(h, h->ortho_plan, m, hp, static_cast<hipStream_t>(stream));
+    return run(h, m, hp, static_cast<hipStream_t>(stream), nullptr);
 }
 
 namespace {
 
-muon_status build_adam_plan(muon_handle* h, AdamPlan& p, const muon_adamw_tensor* ts, int n,
-                            const std::vector<int64_t>& key, hipStream_t stream) {
-    if (p.valid || p.d_desc) {
-        hipError_t e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(h, e, "hipDeviceSynchronize before re-plan");
-        free_adam_plan(p);
-    }
+muon_status build_adam_plan(muon_handle* h, const muon_adamw_tensor* ts, int n, const std::vector<int64_t>& key,
+                            hipStream_t stream, AdamPlan** out) {
     std::vector<AdamChunk> chunks;
     for (int t = 0; t < n; ++t)
         for (int64_t b = 0; b < ts[t].numel; b += kAdamChunk) chunks.push_back(AdamChunk{t, 0, b});
     if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
-    AdamPlan q;
-    bool ok = hipMalloc(reinterpret_cast<void**>(&q.d_desc), sizeof(AdamDesc) * size_t(n)) == hipSuccess &&
-              hipMalloc(reinterpret_cast<void**>(&q.d_chunks), sizeof(AdamChunk) * std::max<size_t>(chunks.size(), 1)) ==
-                  hipSuccess;
-    for (int i = 0; ok && i < kStageSlots; ++i)
-        ok = hipHostMalloc(reinterpret_cast<void**>(&q.h_stage[i]), sizeof(AdamDesc) * size_t(n), hipHostMallocDefault) ==
-                 hipSuccess &&
-             hipEventCreateWithFlags(&q.stage_ev[i], hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
+    std::unique_ptr<AdamPlan> q(new (std::nothrow) AdamPlan());
+    if (!q) return fail(h, MUON_ERR_OOM, "AdamW plan allocation failed");
+    if (hipMalloc(reinterpret_cast<void**>(&q->d_chunks), sizeof(AdamChunk) * std::max<size_t>(chunks.size(), 1)) !=
+        hipSuccess) {
         (void)hipGetLastError();
-        free_adam_plan(q);
+        free_adam_plan(*q);
         return fail(h, MUON_ERR_OOM, "AdamW plan allocation failed");
+    }
+    muon_status st = alloc_staging(h, q->tabs.stage, sizeof(AdamDesc) * size_t(n));
+    if (st != MUON_OK) {
+        free_adam_plan(*q);
+        return st;
     }
     hipError_t e = hipSuccess;
     if (!chunks.empty()) {
-        e = hipMemcpyAsync(q.d_chunks, chunks.data(), sizeof(AdamChunk) * chunks.size(), hipMemcpyHostToDevice, stream);
+        e = hipMemcpyAsync(q->d_chunks, chunks.data(), sizeof(AdamChunk) * chunks.size(), hipMemcpyHostToDevice, stream);
         if (e == hipSuccess) e = hipStreamSynchronize(stream);   // the host vector dies with this call
     }
     if (e != hipSuccess) {
-        free_adam_plan(q);
+        free_adam_plan(*q);
         return hip_fail(h, e, "AdamW plan upload");
     }
-    q.n = n;
-    q.n_chunks = int(chunks.size());
-    q.key = key;
-    q.valid = true;
-    p = std::move(q);
+    q->n = n;
+    q->n_chunks = int(chunks.size());
+    q->key = key;
+    AdamPlan* raw = q.get();
+    h->adam_plans[key] = std::move(q);
+    *out = raw;
     return MUON_OK;
 }
 
@@ -763,11 +921,22 @@ muon_status muon_adamw_step(muon_handle* h, const muon_adamw_tensor* ts, int32_t
         key.push_back(ts[i].numel);
         key.push_back(ts[i].dtype);
     }
-    AdamPlan& plan = h->adam_plan;
-    if (!plan.valid || plan.key != key) {
-        muon_status st = build_adam_plan(h, plan, ts, n, key, s);
-        if (st != MUON_OK) return st;
+    bool capturing = false;
+    muon_status cst = capture_state(h, s, &capturing);
+    if (cst != MUON_OK) return cst;
+    AdamPlan* pp = nullptr;
+    auto pit = h->adam_plans.find(key);
+    if (pit != h->adam_plans.end()) {
+        pp = pit->second.get();
+    } else {
+        if (capturing)
+            return fail(h, MUON_ERR_INVALID_ARG,
+                        "a call captured into a HIP graph must first run once outside capture with the same sizes "
+                        "and pointers (its plan and descriptor table are then resident)");
+        cst = build_adam_plan(h, ts, n, key, s, &pp);
+        if (cst != MUON_OK) return cst;
     }
+    AdamPlan& plan = *pp;
     std::vector<AdamDesc> desc(static_cast<size_t>(n));
     for (int i = 0; i < n; ++i) {
         const muon_adamw_tensor& t = ts[i];
@@ -783,22 +952,10 @@ muon_status muon_adamw_step(muon_handle* h, const muon_adamw_tensor* ts, int32_t
         auto al = [](const void* q, uintptr_t b) { return (reinterpret_cast<uintptr_t>(q) % b) == 0; };
         d.vec = al(t.param, pa) && al(t.grad, pa) && al(t.exp_avg, 16) && al(t.exp_avg_sq, 16);
     }
+    const AdamDesc* d_desc = nullptr;
+    cst = select_table(h, plan.tabs, desc, capturing, s, &d_desc);
+    if (cst != MUON_OK) return cst;
     hipError_t e;
-    if (!plan.have_uploaded || std::memcmp(desc.data(), plan.uploaded.data(), sizeof(AdamDesc) * size_t(n)) != 0) {
-        const int sl = plan.slot;
-        if (plan.stage_used[sl]) {
-            e = hipEventSynchronize(plan.stage_ev[sl]);
-            if (e != hipSuccess) return hip_fail(h, e, "AdamW descriptor staging wait");
-        }
-        std::memcpy(plan.h_stage[sl], desc.data(), sizeof(AdamDesc) * size_t(n));
-        e = hipMemcpyAsync(plan.d_desc, plan.h_stage[sl], sizeof(AdamDesc) * size_t(n), hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipEventRecord(plan.stage_ev[sl], s);
-        if (e != hipSuccess) return hip_fail(h, e, "AdamW descriptor upload");
-        plan.stage_used[sl] = true;
-        plan.slot = (sl + 1) % kStageSlots;
-        plan.uploaded = desc;
-        plan.have_uploaded = true;
-    }
     // bias corrections in double, then the per-call constants in float
     const double bc1 = 1.0 - std::pow(double(hp->beta1), double(hp->step));
     const double bc2 = 1.0 - std::pow(double(hp->beta2), double(hp->step));
@@ -812,7 +969,7 @@ muon_status muon_adamw_step(muon_handle* h, const muon_adamw_tensor* ts, int32_t
     a.inv_sqrt_bc2 = float(1.0 / std::sqrt(bc2));
     a.eps = hp->eps;
     e = timed(h, K_ADAMW, [&](hipEvent_t e0, hipEvent_t e1) {
-        return launch_adamw(plan.d_chunks, plan.n_chunks, plan.d_desc, a, s, e0, e1);
+        return launch_adamw(plan.d_chunks, plan.n_chunks, d_desc, a, s, e0, e1);
     });
     if (e != hipSuccess) return hip_fail(h, e, "adamw launch");
     return MUON_OK;
@@ -820,13 +977,15 @@ muon_status muon_adamw_step(muon_handle* h, const muon_adamw_tensor* ts, int32_t
 
 muon_status muon_read_norms(muon_handle* h, float* out, int32_t n, void* stream) {
     if (!h || !out || n < 0) return MUON_ERR_INVALID_ARG;
-    if (!h->step_plan.valid || n > h->step_plan.n) return fail(h, MUON_ERR_INVALID_ARG, "no step with %d matrices yet", n);
+    if (!h->last_step || n > h->last_step_n) return fail(h, MUON_ERR_INVALID_ARG, "no step with %d matrices yet", n);
     if (n == 0) return MUON_OK;
     DeviceGuard g(h->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(out, h->step_plan.d_nu, sizeof(float) * n, hipMemcpyDeviceToHost, s);
+    std::vector<NormScale> buf(static_cast<size_t>(n));
+    hipError_t e = hipMemcpyAsync(buf.data(), h->last_step->d_norm, sizeof(NormScale) * n, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(h, e, "norm readback");
+    for (int i = 0; i < n; ++i) out[i] = buf[size_t(i)].nu;
     return MUON_OK;
 }
 
@@ -866,7 +1025,9 @@ void muon_kernel_stats_reset(muon_handle* h) {
 
 int64_t muon_workspace_bytes(const muon_handle* h) {
     if (!h) return 0;
-    return int64_t(h->step_plan.ws_bytes + h->ortho_plan.ws_bytes);
+    int64_t b = 0;
+    for (const auto& kv : h->plans) b += int64_t(kv.second->ws_bytes);
+    return b;
 }
 
 muon_status muon_destroy(muon_handle* h) {
@@ -874,9 +1035,8 @@ muon_status muon_destroy(muon_handle* h) {
     {
         DeviceGuard g(h->device);
         (void)hipDeviceSynchronize();
-        free_plan(h->step_plan);
-        free_plan(h->ortho_plan);
-        free_adam_plan(h->adam_plan);
+        for (auto& kv : h->plans) free_plan(*kv.second);
+        for (auto& kv : h->adam_plans) free_adam_plan(*kv.second);
         for (const Pending& p : h->pending) {
             (void)hipEventDestroy(p.a);
             (void)hipEventDestroy(p.b);

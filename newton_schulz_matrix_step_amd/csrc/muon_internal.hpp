@@ -12,6 +12,11 @@ namespace muon {
 // contribute zeros to every contraction.
 constexpr int kPad = 128;
 
+// Entries with min(R, C) at most this run the iteration in float32 in either
+// compute mode: their products cost next to nothing, and with few singular
+// values bf16 operands cost them the most accuracy.
+constexpr int kSmallM = 64;
+
 // Per-matrix descriptor, one entry per matrix of the call, in device memory.
 // "Stored" = the caller's orientation (R x C); "NS" = the m x n orientation the
 // iteration works in (m = min(R, C) rows, transposed when R > C).
@@ -28,7 +33,7 @@ struct MatDesc {
     int32_t vec_ok;            // momentum pass: 8-element vectors legal for grad/mom
     int32_t vec_io;            // epilogues: 4-element vectors legal for param/grad/mom/upd
     float shape_scale;         // sqrt(max(1, R / C))
-    int32_t pad0;
+    int32_t f32;               // the iteration runs in float32 (workspace buffers float32)
     int64_t off_u;             // workspace byte offsets
     int64_t off_xlo;           // bf16 mode: X - bf16(X) in one byte per element; with the operand copy, the master X
     int64_t off_xb0, off_xb1;  // operand copies of X, ping-pong
@@ -52,9 +57,22 @@ struct Tile {
 
 enum PhaseKind : int { PH_GRAM = 0, PH_POLY = 1, PH_AXPY = 2, PH_AXPY_LAST = 3 };
 
+// Norm of one plan entry's input and the scales derived from it (norm
+// finalize kernel).  The operand copy of u is kept as u 2^-k: k = 0 while
+// nu lies in [2^-30, 2^30], where the products of the first iteration can
+// neither overflow nor lose their terms to underflow in float32; outside it the
+// rescale pass multiplies the copy by 2^-k (exact) with k the exponent of nu,
+// and the first iteration applies first = 2^k / (nu + eps) to it.
+struct NormScale {
+    float inv;                 // 1 / (nu + eps)
+    float first;               // 2^k / (nu + eps): scale of X0 relative to the operand copy
+    int32_t k;                 // the operand copy holds u 2^-k
+    float nu;                  // ||u||_F
+};
+
 struct PhaseArgs {
     char* ws;
-    const float* inv_norm;     // per matrix 1 / (||u||_F + eps)
+    const NormScale* norm;     // per matrix
     float a, b, c;
     float lr, wd, beta;
     int32_t iter;              // 1-based iteration index
@@ -63,7 +81,7 @@ struct PhaseArgs {
 
 struct MomentumArgs {
     char* ws;
-    float* partials;           // one sum of squares per unit
+    double* partials;          // one sum of squares per unit
     float beta;
     int32_t nesterov;
 };
@@ -72,11 +90,15 @@ struct MomentumArgs {
 // when not null, are recorded by the dispatch itself at the kernel's start and
 // end (hipExtLaunchKernelGGL), which adds no packets to the stream.
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
-hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a,
-                           bool f32_compute, hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
-hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials,
-                                float* inv_norm, float* nu, float eps, hipStream_t s,
+hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a, hipStream_t s,
+                           hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const double* partials,
+                                NormScale* norm, float eps, hipStream_t s,
                                 hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// Multiplies the operand copy of every entry with k != 0 by 2^-k (one
+// workgroup per momentum-pass unit; the others return at once).
+hipError_t launch_rescale(const Unit* units, int n_units, const MatDesc* mats, const NormScale* norm, char* ws,
+                          hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* tiles, int n_tiles,
                            const MatDesc* mats, PhaseArgs a, hipStream_t s,
                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);

@@ -48,6 +48,12 @@ __device__ __forceinline__ GMEM T* gm(T* p) { return (GMEM T*)p; }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+// Streaming (nontemporal) 16-byte accesses for data a kernel touches once.
+template <class T>
+__device__ __forceinline__ T ld_nt(const GMEM T* p) { return __builtin_nontemporal_load(p); }
+template <class T>
+__device__ __forceinline__ void st_nt(GMEM T* p, T v) { __builtin_nontemporal_store(v, p); }
+
 // Round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     __bf16 h = (__bf16)f;
@@ -89,19 +95,19 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float v) 
         gm(static_cast<float*>(p))[i] = v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
 }
 
 // Sum over the 256 threads of a block in a fixed order; result valid in thread 0.
-__device__ __forceinline__ float block_sum(float v, float* red) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) red[wave] = v;
     __syncthreads();
-    float t = 0.f;
+    double t = 0.0;
     if (threadIdx.x == 0) t = ((red[0] + red[1]) + red[2]) + red[3];
     return t;
 }
@@ -126,12 +132,33 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(u32x4_t* p, size_t 
 // ---------------------------------------------------------------------------
 // momentum + operand copy + partial sums of squares
 // ---------------------------------------------------------------------------
-template <bool F32C>
+// The sum of squares runs in double: u^2 of any finite float is finite there,
+// and the sum of 2^31 of them neither overflows nor loses the small terms, so
+// the norm is right at every gradient scale.  g and m are read once and m' is
+// written once (streaming accesses); the operand copy of u is read again by
+// the first iteration's products.
+#ifndef MUON_MOM_NT_U
+#define MUON_MOM_NT_U 0
+#endif
+#ifndef MUON_MOM_NT
+#define MUON_MOM_NT 1
+#endif
+template <class T>
+__device__ __forceinline__ T mom_ld(const GMEM T* p) {
+    if (MUON_MOM_NT) return ld_nt(p);
+    return *p;
+}
+template <class T>
+__device__ __forceinline__ void mom_st(GMEM T* p, T v) {
+    if (MUON_MOM_NT) st_nt(p, v);
+    else *p = v;
+}
 __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restrict__ units,
                                                             const MatDesc* __restrict__ mats, MomentumArgs ka) {
-    __shared__ float red[4];
+    __shared__ double red[4];
     const Unit un = units[blockIdx.x];
     const MatDesc& md = mats[un.mat];
+    const bool F32C = md.f32 != 0;   // this entry's iteration runs in float32
     const int C = md.C;
     const int rows = un.r1 - un.r0;
     const float beta = ka.beta;
@@ -139,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
     const bool has_mom = md.has_mom != 0;
     char* ub = ka.ws + md.off_u;
     const int64_t ldu = md.Cp;
-    float ss = 0.f;
+    double ss = 0.0;
 
     if (md.vec_ok) {
         // kU groups of 8 columns per thread per pass: every load of the pass is
@@ -166,16 +193,16 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
                 col[u] = (idx - rr * gpr) << 3;
                 if (idx < total) {
                     if (bf) {
-                        graw[u][0] = *reinterpret_cast<const GMEM u32x4_t*>(gbase + (row[u] * md.ld_grad + col[u]) * 2);
+                        graw[u][0] = mom_ld(reinterpret_cast<const GMEM u32x4_t*>(gbase + (row[u] * md.ld_grad + col[u]) * 2));
                     } else {
                         const GMEM u32x4_t* gp = reinterpret_cast<const GMEM u32x4_t*>(gbase + (row[u] * md.ld_grad + col[u]) * 4);
-                        graw[u][0] = gp[0];
-                        graw[u][1] = gp[1];
+                        graw[u][0] = mom_ld(gp);
+                        graw[u][1] = mom_ld(gp + 1);
                     }
                     if (has_mom) {
                         const GMEM f32x4_t* mp = reinterpret_cast<const GMEM f32x4_t*>(mbase + row[u] * md.ld_mom + col[u]);
-                        mv[u][0] = mp[0];
-                        mv[u][1] = mp[1];
+                        mv[u][0] = mom_ld(mp);
+                        mv[u][1] = mom_ld(mp + 1);
                     }
                 }
             }
@@ -206,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
                         m1[q] = fmaf(beta, m1[q], g[4 + q]);
                     }
                     GMEM f32x4_t* mp = reinterpret_cast<GMEM f32x4_t*>(mbase + row[u] * md.ld_mom + col[u]);
-                    mp[0] = m0;
-                    mp[1] = m1;
+                    mom_st(mp, m0);
+                    mom_st(mp + 1, m1);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         uu[q] = nest ? fmaf(beta, m0[q], g[q]) : m0[q];
@@ -218,16 +245,23 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
                     for (int q = 0; q < 8; ++q) uu[q] = g[q];
                 }
 #pragma unroll
-                for (int q = 0; q < 8; ++q) ss = fmaf(uu[q], uu[q], ss);
+                for (int q = 0; q < 8; ++q) ss = fma(double(uu[q]), double(uu[q]), ss);
                 if (F32C) {
                     GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + row[u] * ldu + col[u]));
-                    up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
-                    up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
+                    if (MUON_MOM_NT_U) {
+                        st_nt(up, f32x4_t{uu[0], uu[1], uu[2], uu[3]});
+                        st_nt(up + 1, f32x4_t{uu[4], uu[5], uu[6], uu[7]});
+                    } else {
+                        up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
+                        up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
+                    }
                 } else {
                     u32x4_t w;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(uu[2 * q], uu[2 * q + 1]);
-                    *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + row[u] * ldu + col[u])) = w;
+                    GMEM u32x4_t* up = gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + row[u] * ldu + col[u]));
+                    if (MUON_MOM_NT_U) st_nt(up, w);
+                    else *up = w;
                 }
             }
         }
@@ -245,28 +279,30 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
                 *mp = mn;
                 u = nest ? fmaf(beta, mn, g) : mn;
             }
-            ss = fmaf(u, u, ss);
+            ss = fma(double(u), double(u), ss);
             if (F32C)
                 gm(reinterpret_cast<float*>(ub))[r * ldu + c] = u;
             else
                 gm(reinterpret_cast<uint16_t*>(ub))[r * ldu + c] = f32_to_bf16(u);
         }
     }
-    const float tot = block_sum(ss, red);
+    const double tot = block_sum(ss, red);
     if (threadIdx.x == 0) ka.partials[blockIdx.x] = tot;
 }
 
 // ---------------------------------------------------------------------------
-// per-matrix norm: fixed-order double sum of the unit partials
+// per-matrix norm: fixed-order double sum of the unit partials, and the
+// power-of-two range of the operand copy (NormScale)
 // ---------------------------------------------------------------------------
+constexpr int kSafeExp = 30;   // nu in [2^-30, 2^30]: operand copy kept as u
+
 __global__ __launch_bounds__(kThreads) void finalize_norm_kernel(const MatDesc* __restrict__ mats,
-                                                                 const float* __restrict__ partials,
-                                                                 float* __restrict__ inv_norm,
-                                                                 float* __restrict__ nu_out, float eps) {
+                                                                 const double* __restrict__ partials,
+                                                                 NormScale* __restrict__ norm, float eps) {
     __shared__ double red[kThreads];
     const MatDesc& md = mats[blockIdx.x];
     double s = 0.0;
-    for (int i = threadIdx.x; i < md.nunits; i += kThreads) s += double(partials[md.unit0 + i]);
+    for (int i = threadIdx.x; i < md.nunits; i += kThreads) s += partials[md.unit0 + i];
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = kThreads / 2; w > 0; w >>= 1) {
@@ -275,8 +311,41 @@ __global__ __launch_bounds__(kThreads) void finalize_norm_kernel(const MatDesc* 
     }
     if (threadIdx.x == 0) {
         const double nu = sqrt(red[0]);
-        inv_norm[blockIdx.x] = float(1.0 / (nu + double(eps)));
-        nu_out[blockIdx.x] = float(nu);
+        int k = 0;
+        if (nu > 0.0 && nu < __builtin_inf() && (nu < 0x1p-30 || nu > 0x1p+30)) k = ilogb(nu);
+        const double inv = 1.0 / (nu + double(eps));
+        NormScale ns;
+        ns.inv = float(inv);
+        ns.first = float(ldexp(inv, k));
+        ns.k = k;
+        ns.nu = float(nu);
+        norm[blockIdx.x] = ns;
+    }
+}
+
+// Operand copy of u -> u 2^-k for the entries whose norm lies outside the
+// safe range (exact: a power-of-two scaling of values far from the ends of
+// the exponent range).
+__global__ __launch_bounds__(kThreads) void rescale_kernel(const Unit* __restrict__ units,
+                                                           const MatDesc* __restrict__ mats,
+                                                           const NormScale* __restrict__ norm, char* ws) {
+    const Unit un = units[blockIdx.x];
+    const int k = norm[un.mat].k;
+    if (k == 0) return;
+    const MatDesc& md = mats[un.mat];
+    const bool F32C = md.f32 != 0;
+    const int C = md.C;
+    const int total = (un.r1 - un.r0) * C;
+    for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+        const int rr = idx / C;
+        const int64_t i = int64_t(un.r0 + rr) * md.Cp + (idx - rr * C);
+        if (F32C) {
+            GMEM float* p = gm(reinterpret_cast<float*>(ws + md.off_u)) + i;
+            *p = ldexpf(*p, -k);
+        } else {
+            GMEM uint16_t* p = gm(reinterpret_cast<uint16_t*>(ws + md.off_u)) + i;
+            *p = f32_to_bf16(ldexpf(bf16_to_f32(*p), -k));
+        }
     }
 }
 
@@ -452,7 +521,7 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
         const char* ain = ws + md.off_a;
         float scl = 1.f;
         if (KIND == PH_GRAM && it == 1) {
-            const float s = pa.inv_norm[t.mat];
+            const float s = pa.norm[t.mat].first;
             scl = s * s;
         }
         const bool diag = t.ti == t.tj;
@@ -478,7 +547,8 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
         // AXPY output tiles cover the stored R x C shape (see resolve_operands)
         const int R = md.R, C = md.C;
         const int64_t ldx = md.Cp;
-        const float alpha = (it == 1) ? pa.inv_norm[t.mat] : 1.f;
+        const float alpha = (it == 1) ? pa.norm[t.mat].first : 1.f;
+        const int k0 = (it == 1) ? pa.norm[t.mat].k : 0;   // the master term is u: scale it like the copy
         const bool nest = pa.nesterov != 0;
         const float* xm = reinterpret_cast<const float*>(ws + off_cur);   // fp32 mode: X itself
         char* xb_next = ws + (((it - 1) & 1) ? md.off_xb1 : md.off_xb0);
@@ -492,7 +562,8 @@ __device__ __forceinline__ void epilogue(const MatDesc& md, const Tile& t, const
                 for (int e = 0; e < 4; ++e) {
                     const int r = gr0 + 16 * i + e, c = gc0 + 16 * j;
                     if (r < R && c < C) {
-                        const float master = (it == 1) ? u_at(md, r, c, pa.beta, nest) : xm[int64_t(r) * ldx + c];
+                        const float master =
+                            (it == 1) ? ldexpf(u_at(md, r, c, pa.beta, nest), -k0) : xm[int64_t(r) * ldx + c];
                         const float v = alpha * fmaf(pa.a, master, acc[i][j][e]);
                         if (KIND == PH_AXPY) {
                             store_elem(xb_next, int64_t(r) * ldx + c, ODT, v);
@@ -613,9 +684,10 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int BM, int BK_ = 64>
 struct BfCfg {
     static constexpr int BK = BK_;                // k per LDS stage (32 or 64)
-    // LDS stages (ring; the epilogue reuses them), within 64 KB so two
-    // workgroups share a CU
-    static constexpr int LDS_BUDGET = 64 * 1024;
+    // LDS stages (ring; the epilogue reuses them): 128-wide tiles within
+    // 64 KB so two workgroups share a CU; 256-wide tiles take the whole
+    // 160 KB of one CU
+    static constexpr int LDS_BUDGET = BM == 256 ? 160 * 1024 : 64 * 1024;
     static constexpr int NST = LDS_BUDGET / (2 * BM * BK * 2) > 8 ? 8 : LDS_BUDGET / (2 * BM * BK * 2);
     static constexpr int CPK = BK / 8;            // 16-byte chunks per [row][BK] row
     static constexpr int WT = BM / 2;             // wave tile edge
@@ -628,6 +700,10 @@ struct BfCfg {
     static constexpr int RPK = 64 / CPR;          // [k][BM] rows per 1 KB
 };
 constexpr int kBK = 64;
+// k per LDS stage: 64 on 128-wide tiles; 32 on 256-wide ones (five stages of
+// 32 KB keep four k blocks of loads in flight)
+template <int BM>
+constexpr int bk_of() { return BM == 256 ? 32 : kBK; }
 
 // Swizzle of the 16-byte chunks of a [k][BM] LDS row.  A ds_read_b64_tr_b16
 // group of 16 lanes reads rows k0..k0+3 (4 rows x 32 bytes): bits 1-2 spread
@@ -929,6 +1005,7 @@ struct AxpyCtx {
     int64_t ldq;
     int R, C;
     bool vio;
+    int k0;                    // first iteration: the operand copy holds u 2^-k0 (NormScale)
     float alpha, a, beta, wdec, step;
     IoView io;
 };
@@ -1074,6 +1151,10 @@ __device__ __forceinline__ void axpy_store(const AxpyCtx& x, const float* __rest
         } else {
             mst = dec4(w.ra[q], io_dt<M>(x.io));
         }
+        if (FIRST) {   // u on the operand copy's scale
+#pragma unroll
+            for (int k = 0; k < 4; ++k) mst[k] = ldexpf(mst[k], -x.k0);
+        }
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + lr * E::LDW + lc);
         const f32x4_t o = x.alpha * (x.a * (mst + v));   // acc holds (B / a) X
         if (!LAST) {
@@ -1153,7 +1234,8 @@ __device__ __forceinline__ AxpyCtx axpy_ctx(const MatDesc& md, const Tile& t, co
     x.R = md.R;
     x.C = md.C;
     x.vio = md.vec_io != 0;
-    x.alpha = FIRST ? pa.inv_norm[t.mat] : 1.f;
+    x.alpha = FIRST ? pa.norm[t.mat].first : 1.f;
+    x.k0 = FIRST ? pa.norm[t.mat].k : 0;
     x.a = pa.a;
     x.beta = pa.beta;
     x.wdec = 1.f - pa.lr * pa.wd;
@@ -1277,7 +1359,7 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     x.diag = t.ti == t.tj;
     x.scl = 1.f;
     if (KIND == PH_GRAM && pa.iter == 1) {
-        const float sn = pa.inv_norm[t.mat];
+        const float sn = pa.norm[t.mat].first;
         x.scl = sn * sn;
     }
     // the bf16 AXPY accumulates on top of the unscaled master X, so POLY
@@ -1332,10 +1414,11 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
-__global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restrict__ tiles,
+__global__ __launch_bounds__(kThreads, BM == 128 ? 2 : 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
                                                             const MatDesc* __restrict__ mats, PhaseArgs pa,
                                                             int n_tiles) {
-    using C = BfCfg<BM, kBK>;
+    constexpr int BK = bk_of<BM>();
+    using C = BfCfg<BM, BK>;
     constexpr int TI = C::TI, WT = C::WT;
     // operand stages; afterwards the epilogue's per-wave regions
     constexpr int EPI_AXPY_BYTES = 16 * (WT + 4) * 4;
@@ -1385,9 +1468,9 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restri
             constexpr int CAPV = decltype(capc)::value;
             constexpr bool AKC_ALL = decltype(akc)::value;
             if constexpr (PRE > 0)
-                mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap, pre);
+                mainloop<BM, BK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap, pre);
             else
-                mainloop<BM, kBK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+                mainloop<BM, BK, true, AKC_ALL, false, CAPV>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
         };
         if (op.a_kc && op.b_kc) {   // transposed matrix: X^T B, X is the A operand
             cap.kb = (row_b0 + wc) / kBK;
@@ -1405,11 +1488,11 @@ __global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restri
         constexpr bool CAPA = KIND == PH_POLY && WT == kBK;
         if constexpr (KIND == PH_POLY) {
             cap.kb = (row_b0 + wc) / kBK;
-            mainloop<BM, kBK, true, true, true, CAPA ? 3 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
+            mainloop<BM, BK, true, true, true, CAPA ? 3 : 0>(smem, op, row_a0, row_b0, wave, lane, acc, &cap);
         } else if (op.a_kc && op.b_kc) {
-            mainloop<BM, kBK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, BK, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         } else {
-            mainloop<BM, kBK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+            mainloop<BM, BK, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc);
         }
         __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
         epi_sym<KIND, TI, CAPA>(md, t, pa, acc, cap, row_a0 + wr, row_b0 + wc, lane, smem + wave * EPI_SYM_BYTES);
@@ -1425,7 +1508,7 @@ __global__ __launch_bounds__(kThreads) void direct_update_kernel(const Unit* __r
     const MatDesc& md = mats[un.mat];
     const int C = md.C;
     const int total = (un.r1 - un.r0) * C;
-    const float s = pa.inv_norm[un.mat];
+    const float s = pa.norm[un.mat].inv;
     const float wdec = 1.f - pa.lr * pa.wd;
     const float step = pa.lr * md.shape_scale;
     const bool nest = pa.nesterov != 0;
@@ -1456,21 +1539,25 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a, bool f32c,
-                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a, hipStream_t s,
+                           hipEvent_t ev0, hipEvent_t ev1) {
     if (n_units <= 0) return hipSuccess;
-    if (f32c)
-        hipExtLaunchKernelGGL(momentum_kernel<true>, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
-    else
-        hipExtLaunchKernelGGL(momentum_kernel<false>, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
+    hipExtLaunchKernelGGL(momentum_kernel, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, a);
     return hipGetLastError();
 }
 
-hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const float* partials, float* inv_norm, float* nu,
-                                float eps, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const double* partials, NormScale* norm, float eps,
+                                hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_mats <= 0) return hipSuccess;
-    hipExtLaunchKernelGGL(finalize_norm_kernel, dim3(n_mats), dim3(kThreads), 0, s, ev0, ev1, 0, mats, partials,
-                          inv_norm, nu, eps);
+    hipExtLaunchKernelGGL(finalize_norm_kernel, dim3(n_mats), dim3(kThreads), 0, s, ev0, ev1, 0, mats, partials, norm,
+                          eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rescale(const Unit* units, int n_units, const MatDesc* mats, const NormScale* norm, char* ws,
+                          hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (n_units <= 0) return hipSuccess;
+    hipExtLaunchKernelGGL(rescale_kernel, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, norm, ws);
     return hipGetLastError();
 }
 
@@ -1490,25 +1577,28 @@ static void launch_bf16(bool first, const Tile* tiles, int n_tiles, const MatDes
 }
 
 template <int KIND>
-static void launch_kind(bool f32c, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a, hipStream_t s,
-                        hipEvent_t ev0, hipEvent_t ev1) {
+static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats, PhaseArgs a,
+                        hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (f32c) {
         hipExtLaunchKernelGGL((ns_gemm_kernel<KIND, true>), dim3(n_tiles), dim3(kThreads), 0, s, ev0, ev1, 0, tiles,
                               mats, a);
         return;
     }
-    launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
+    if (tile == 256)
+        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
+    else
+        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    if (tile != 128) return hipErrorInvalidValue;
+    if (tile != 128 && !(tile == 256 && !f32c)) return hipErrorInvalidValue;
     switch (kind) {
-        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_POLY: launch_kind<PH_POLY>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
-        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY: launch_kind<PH_AXPY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
+        case PH_AXPY_LAST: launch_kind<PH_AXPY_LAST>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -1,14 +1,16 @@
 // Test infrastructure: runs muon_step and muon_adamw_step of the library, built
 // against the CPU stand-in of HIP (tests/emu/hip), on exactly sized host
 // buffers, so AddressSanitizer reports any access outside a caller buffer or
-// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT]]]
+// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT [GRAD]]]]
 //   SHAPES "RxC,RxC,...", DTYPE 0 = bf16, 1 = f32 (also selects fp32 compute),
 //   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks,
 //   LD_PAD extra elements per row (views into wider buffers), SHIFT elements
 //   by which every buffer starts past its allocation (unaligned bases).
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstdlib>
+#include <cstring>
 #include <string>
 #include <vector>
 
@@ -27,6 +29,7 @@ int main(int argc, char** argv) {
     const int block_rows = argc > 4 ? std::atoi(argv[4]) : 0;
     const long pad = argc > 5 ? std::atol(argv[5]) : 0;
     const long shift = argc > 6 ? std::atol(argv[6]) : 0;
+    const double gval = argc > 7 ? std::atof(argv[7]) : 0.0;
     std::vector<std::pair<long, long>> shapes;
     for (size_t p = 0; p < spec.size();) {
         size_t q = spec.find(',', p);
@@ -48,7 +51,19 @@ int main(int argc, char** argv) {
         muon_matrix m{};
         const long ld = c + pad;
         m.param = buf(r, ld, c, es);
-        m.grad = buf(r, ld, c, es);
+        void* g = buf(r, ld, c, es);
+        for (long i = 0; i < r; ++i)
+            for (long j = 0; j < c; ++j) {
+                const float v = float(gval);
+                if (es == 4) {
+                    static_cast<float*>(g)[i * ld + j] = v;
+                } else {
+                    uint32_t u;
+                    std::memcpy(&u, &v, 4);
+                    static_cast<uint16_t*>(g)[i * ld + j] = uint16_t(u >> 16);
+                }
+            }
+        m.grad = g;
         m.momentum = static_cast<float*>(buf(r, ld, c, 4));
         m.update_out = static_cast<float*>(buf(r, ld, c, 4));
         m.rows = r;

@@ -58,10 +58,15 @@ inline hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 inline hipError_t hipEventDestroy(hipEvent_t) { return hipSuccess; }
 inline hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) { *ms = 0; return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
+enum hipStreamCaptureStatus { hipStreamCaptureStatusNone = 0, hipStreamCaptureStatusActive = 1 };
+inline hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* s) {
+    *s = hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
 inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
 
 inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
-inline float __shfl_xor(float v, int, int) { return v; }
+template <class T> inline T __shfl_xor(T v, int, int) { return v; }
 inline void __syncthreads() {}
 
 #define __builtin_amdgcn_readfirstlane(x) (x)

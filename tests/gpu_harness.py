@@ -16,11 +16,63 @@ from muon_synth import Workload, encode_storage, make_grad, make_momentum, make_
 TOL_O_BF16 = 3e-2        # orthogonalised update, bf16 MFMA mode
 TOL_O_FP32 = 1e-5        # orthogonalised update, fp32 validation mode
 TOL_MOM = 1e-6           # momentum buffers, fp32 storage
+# Local bars on O: every 128 x 128 tile of the stored R x C output (the AXPY
+# kernel's output tiles), every row of at least LOCAL_MIN_LINE elements and
+# every such column must meet the whole-matrix bar on its own, each measured
+# against at least its fair share of the whole norm (sqrt(elements / R C)
+# ||O||_F), so a tile whose own norm is tiny is not held to a relative bar it
+# cannot meet.  One wrong tile, row or column of a large matrix moves the
+# whole-matrix error by only ~1e-2 but its own by ~1.
+LOCAL_TILE = 128
+LOCAL_MIN_LINE = 64
 
 
 def relf(x: np.ndarray, y: np.ndarray) -> float:
     d = np.linalg.norm(np.asarray(x, np.float64) - np.asarray(y, np.float64))
     return float(d / max(np.linalg.norm(np.asarray(y, np.float64)), 1e-300))
+
+
+def local_errors(o: np.ndarray, ref: np.ndarray, tile: int = LOCAL_TILE, min_line: int = LOCAL_MIN_LINE) -> dict:
+    """Worst local error ratios of ``o`` against ``ref`` (both R x C):
+    ||dO_part||_F / max(||ref_part||_F, sqrt(|part| / RC) ||ref||_F) over the
+    tile x tile tiles (clipped at the edges), the rows of at least
+    ``min_line`` elements and the columns of at least ``min_line`` elements
+    (0.0 where a matrix has no such line)."""
+    o = np.asarray(o, np.float64)
+    ref = np.asarray(ref, np.float64)
+    R, C = ref.shape
+    n = float(R * C)
+    tot = float(np.linalg.norm(ref))
+    d = o - ref
+    rt = int(np.ceil(R / tile))
+    ct = int(np.ceil(C / tile))
+    pad_r, pad_c = rt * tile - R, ct * tile - C
+    dp = np.pad(d, ((0, pad_r), (0, pad_c))).reshape(rt, tile, ct, tile)
+    rp = np.pad(ref, ((0, pad_r), (0, pad_c))).reshape(rt, tile, ct, tile)
+    dn = np.sqrt(np.einsum("iajb,iajb->ij", dp, dp))
+    rn = np.sqrt(np.einsum("iajb,iajb->ij", rp, rp))
+    hr = np.minimum(tile, R - tile * np.arange(rt))[:, None]
+    hc = np.minimum(tile, C - tile * np.arange(ct))[None, :]
+    floor = np.sqrt(hr * hc / n) * tot
+    out = {"tile": float(np.max(dn / np.maximum(np.maximum(rn, floor), 1e-300))), "row": 0.0, "col": 0.0}
+    if C >= min_line:
+        fl = np.sqrt(C / n) * tot
+        out["row"] = float(np.max(np.linalg.norm(d, axis=1) /
+                                  np.maximum(np.maximum(np.linalg.norm(ref, axis=1), fl), 1e-300)))
+    if R >= min_line:
+        fl = np.sqrt(R / n) * tot
+        out["col"] = float(np.max(np.linalg.norm(d, axis=0) /
+                                  np.maximum(np.maximum(np.linalg.norm(ref, axis=0), fl), 1e-300)))
+    return out
+
+
+def assert_o_close(o_gpu: np.ndarray, o_ref: np.ndarray, tol: float, what: str) -> dict:
+    """Whole-matrix rel-F and every local ratio (tiles, rows, columns) within
+    ``tol``; returns the figures."""
+    e = {"global": relf(o_gpu, o_ref), **local_errors(o_gpu, o_ref)}
+    for k, v in e.items():
+        assert v <= tol, f"{what}: O {k} error {v:.3e} > {tol}"
+    return e
 
 
 def to_device(stored: np.ndarray, dev="cuda"):
@@ -148,11 +200,15 @@ def check_against_oracle(wl: Workload, rec: Dict[int, List[StepRecord]], tol_o: 
                 res = oracle.muon_step_matrix_blocked(w_old, g, m, hp, *blk)
             e_m = relf(r.m_new, res.m)
             e_o = relf(r.o, res.o)
+            loc = local_errors(r.o, res.o)
             if report is not None:
                 report.append((i, s + 1, e_m, e_o))
-            print(f"  matrix {i} {r.w_old.shape} step {s + 1}: mom {e_m:.2e}  O {e_o:.2e}", flush=True)
+            print(f"  matrix {i} {r.w_old.shape} step {s + 1}: mom {e_m:.2e}  O {e_o:.2e}  (tile {loc['tile']:.2e}, "
+                  f"row {loc['row']:.2e}, col {loc['col']:.2e})", flush=True)
             assert e_m <= TOL_MOM, f"matrix {i} step {s + 1}: momentum rel err {e_m:.3e}"
             assert e_o <= tol_o, f"matrix {i} step {s + 1}: O rel err {e_o:.3e} > {tol_o}"
+            for k, v in loc.items():
+                assert v <= tol_o, f"matrix {i} step {s + 1}: O {k} error {v:.3e} > {tol_o}"
             # the stored weight: float64 update of the GPU's own O, rounded once
             sc = shape_scales(r.w_old.shape, blk)
             w_exp = w_old * (1.0 - wl.lr * wl.weight_decay) - wl.lr * sc * r.o.astype(np.float64)

@@ -143,6 +143,41 @@ def test_adamw_hparams_marshalling():
 def test_profile_role_flags(lib):
     assert nsm.profile_roles(["ns_axpy"]) == 1 << (16 + 4)
     assert nsm.profile_roles(["momentum_norm", "adamw"]) == (1 | 1 << 8) << 16
+    assert nsm.profile_roles(["norm_rescale"]) == 1 << (16 + 9)
     h = ctypes.c_void_p()
     # role bits beyond the last role are unknown flag bits: rejected before any device query
-    assert lib.muon_init(ctypes.byref(h), 0, nsm.MUON_INIT_PROFILE | (1 << (16 + 9))) == nsm.MUON_ERR_INVALID_ARG
+    assert lib.muon_init(ctypes.byref(h), 0, nsm.MUON_INIT_PROFILE | (1 << (16 + 10))) == nsm.MUON_ERR_INVALID_ARG
+
+
+def test_binding_checks_shapes_dtypes_and_devices():
+    """The C ABI sees only pointers and sizes, so the binding rejects tensors
+    whose sizes or dtypes the kernels would read or write past (a smaller or
+    bf16 momentum, a mismatched update_out), and tensors off the GPU, before
+    anything reaches the library."""
+    import torch
+    w = torch.zeros(8, 12, dtype=torch.bfloat16)
+    g = torch.zeros(8, 12, dtype=torch.bfloat16)
+    m = torch.zeros(8, 12)
+    bad = [
+        ((w, g, torch.zeros(8, 12, dtype=torch.bfloat16)), "float32"),   # bf16 momentum
+        ((w, g, torch.zeros(8, 11)), "shape"),                           # smaller momentum
+        ((w, torch.zeros(12, 8, dtype=torch.bfloat16), m), "shape"),     # transposed grad
+        ((w, g, m, torch.zeros(8, 12, dtype=torch.bfloat16)), "float32"),  # bf16 update_out
+        ((w, g, m, torch.zeros(4, 12)), "shape"),                        # smaller update_out
+        ((torch.zeros(96, dtype=torch.bfloat16), g, m), "2-D"),
+        ((w, g, m), "GPU"),                                              # all on the host
+    ]
+    for args, what in bad:
+        with pytest.raises(ValueError, match=what):
+            nsm.make_matrix(*args)
+    with pytest.raises(ValueError, match="shape"):
+        nsm.muon_orthogonalize(0, g, torch.zeros(12, 8), nsm.Hparams())
+    with pytest.raises(ValueError, match="float32"):
+        nsm.muon_orthogonalize(0, g, torch.zeros(8, 12, dtype=torch.bfloat16), nsm.Hparams())
+    with pytest.raises(ValueError, match="GPU"):
+        nsm.muon_orthogonalize(0, g, torch.zeros(8, 12), nsm.Hparams())
+    z = torch.zeros(100)
+    with pytest.raises(ValueError, match="GPU"):
+        nsm.make_adamw_tensor(z, z.clone(), z.clone(), z.clone())
+    with pytest.raises(ValueError, match="float32"):
+        nsm.make_adamw_tensor(z, z.clone(), z.clone().double(), z.clone())

@@ -17,7 +17,8 @@ EMU = os.path.join(ROOT, "tests", "emu")
 CXX = "/opt/rocm/lib/llvm/bin/clang++"
 
 CASES = [
-    # shapes, ns_steps, dtype (0 bf16, 1 f32), block rows, leading-dimension pad, misaligned start
+    # shapes, ns_steps, dtype (0 bf16, 1 f32), block rows, leading-dimension pad, misaligned start,
+    # gradient value (1e15: every norm beyond 2^30, so the rescale pass runs)
     ("300x100,100x300,256x256,129x515,515x129,64x64,1x17,17x1,200x199", 3, 0, 0),
     ("300x100,100x300,129x515,515x129,1x17,17x1,200x199", 2, 0, 0, 5, 1),
     ("300x100,100x300,129x515,33x64", 2, 1, 0, 8, 3),
@@ -27,16 +28,22 @@ CASES = [
     ("100x300,300x100", 0, 0, 0),
     ("768x256,384x96,130x60", 1, 0, 128),
     ("384x96,130x60", 2, 0, 65),
+    ("300x100,100x300,129x515,515x129,64x64,1x17,17x1,200x199", 2, 0, 0, 0, 0, 1e15),
+    ("300x100,100x300,129x515,33x64", 2, 1, 0, 5, 1, 1e15),
 ]
 
 
-@pytest.fixture(scope="module")
-def emu_binary(tmp_path_factory):
+# the same cases with the planner's 256 x 256 tiles on every bf16 entry of 65
+# rows and columns or more (the library's default sends only large ones there)
+WIDE_CASES = [c for c in CASES if c[2] == 0]
+
+
+def _build(tmp_path_factory, name, extra):
     if not os.path.exists(CXX):
         pytest.skip("ROCm clang++ not available")
-    out = tmp_path_factory.mktemp("emu")
+    out = tmp_path_factory.mktemp(name)
     flags = ["-O1", "-g", "-std=c++17", "-fsanitize=address", "-fno-omit-frame-pointer", f"-I{EMU}",
-             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wno-unused-value"]
+             f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wno-unused-value", *extra]
     objs = []
     for src, lang in (("muon_kernels.hip", ["-x", "c++"]), ("adamw_kernels.hip", ["-x", "c++"]),
                       ("muon_api.cpp", [])):
@@ -50,10 +57,29 @@ def emu_binary(tmp_path_factory):
     return exe
 
 
-@pytest.mark.parametrize("case", CASES)
-def test_kernels_stay_in_bounds(emu_binary, case):
+@pytest.fixture(scope="module")
+def emu_binary(tmp_path_factory):
+    return _build(tmp_path_factory, "emu", [])
+
+
+@pytest.fixture(scope="module")
+def emu_binary_wide(tmp_path_factory):
+    return _build(tmp_path_factory, "emu_wide", ["-DMUON_WIDE_MIN_M=65"])
+
+
+def _run(exe, case):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
-    r = subprocess.run([emu_binary, *[str(v) for v in case]], capture_output=True, text=True, env=env, timeout=600)
+    r = subprocess.run([exe, *[str(v) for v in case]], capture_output=True, text=True, env=env, timeout=900)
     assert "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
     assert r.returncode == 0, (r.stdout, r.stderr[-2000:])
     assert "step 0" in r.stdout and "adamw 0" in r.stdout
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_kernels_stay_in_bounds(emu_binary, case):
+    _run(emu_binary, case)
+
+
+@pytest.mark.parametrize("case", WIDE_CASES)
+def test_wide_tile_kernels_stay_in_bounds(emu_binary_wide, case):
+    _run(emu_binary_wide, case)
