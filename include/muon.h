@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 5
+#define MUON_ABI_VERSION 6
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -209,6 +209,32 @@ muon_status muon_init(muon_handle **out, int device, uint32_t flags);
  * MUON_ERR_HIP. */
 muon_status muon_step(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
                       const muon_hparams *hp, void *stream);
+
+/* muon_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same step, with the same arguments, validation, errors and results
+ * (bitwise) as muon_step, but every buffer it needs beyond the caller's
+ * tensors (workspace, tile lists, units, norm partials, descriptor table)
+ * lives in a static device array of 256 MiB per GPU (MUON_STATIC_SCRATCH_BYTES)
+ * that the library reserves when it is loaded and holds until the process
+ * ends.  Nothing is allocated: no hipMalloc/hipFree, no pinned host memory,
+ * no events (profiling handles are not timed here).
+ *   - A call whose workspace and tables exceed the scratch returns
+ *     MUON_ERR_INVALID_ARG naming both sizes and enqueues nothing (roughly: up
+ *     to ~30 M weight elements per call in bf16 mode).
+ *   - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *     call's contents.  A call whose signature differs from the previous call's
+ *     on the device clears the workspace (a fill kernel) and writes its tile
+ *     lists; one whose pointers differ writes its descriptor table; either
+ *     waits for `stream` before returning (the copies read host memory).  A
+ *     call with the previous call's shapes and pointers enqueues kernels only.
+ *   - Calls that overlap on one GPU (other streams, other threads, other
+ *     handles) race on the scratch: order them.
+ *   - The handle is used for its device and error text only; its plans are
+ *     neither used nor created. */
+#define MUON_STATIC_SCRATCH_BYTES (256u << 20)
+muon_status muon_step_noalloc(muon_handle *h, const muon_matrix *mats, int32_t n_mats,
+                              const muon_hparams *hp, void *stream);
 
 /* Newton-Schulz only: out = NS(in) for one rows x cols matrix (normalise,
  * transpose rule, hp->ns_steps iterations with hp->a/b/c and hp->eps, in

@@ -43,6 +43,7 @@ from ._abi import (  # noqa: F401
     muon_read_norms,
     muon_status_str,
     muon_step,
+    muon_step_noalloc,
     muon_step_raw,
     muon_workspace_bytes,
     profile_roles,

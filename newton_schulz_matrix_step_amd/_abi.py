@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence
 # the in-tree build; MUON_LIBRARY names another build of the same library to load instead
 LIB_PATH = os.environ.get("MUON_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                           "libmuon_mi355x.so")
-ABI_VERSION = 5   # the MUON_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 6   # the MUON_ABI_VERSION of the header this binding mirrors
 
 MUON_OK = 0
 MUON_ERR_INVALID_ARG = 1
@@ -50,6 +50,7 @@ EXPORTED_SYMBOLS = (
     "muon_abi_version",
     "muon_init",
     "muon_step",
+    "muon_step_noalloc",
     "muon_adamw_step",
     "muon_orthogonalize",
     "muon_read_norms",
@@ -152,6 +153,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_init.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_uint32]
     lib.muon_step.restype = ctypes.c_int
     lib.muon_step.argtypes = [vp, ctypes.POINTER(muon_matrix), i32, ctypes.POINTER(muon_hparams), vp]
+    lib.muon_step_noalloc.restype = ctypes.c_int
+    lib.muon_step_noalloc.argtypes = [vp, ctypes.POINTER(muon_matrix), i32, ctypes.POINTER(muon_hparams), vp]
     lib.muon_adamw_step.restype = ctypes.c_int
     lib.muon_adamw_step.argtypes = [vp, ctypes.POINTER(muon_adamw_tensor), i32, ctypes.POINTER(muon_adamw_hparams), vp]
     lib.muon_orthogonalize.restype = ctypes.c_int
@@ -300,10 +303,9 @@ def make_matrix(param, grad, momentum, update_out=None, block=(0, 0)) -> muon_ma
         int(block[0]), int(block[1]), 0)
 
 
-def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp: Hparams,
-              update_outs: Optional[Sequence] = None, stream=None, blocks: Optional[Sequence] = None) -> None:
-    """One Muon step over every (param, grad, momentum) triple, on ``stream``;
-    ``blocks[i]`` = (block_rows, block_cols) of matrix i, or None for all (0, 0)."""
+def _matrices(params: Sequence, grads: Sequence, moms: Sequence, update_outs: Optional[Sequence] = None,
+              blocks: Optional[Sequence] = None):
+    """The muon_matrix array of one call."""
     n = len(params)
     if len(grads) != n or len(moms) != n or (update_outs is not None and len(update_outs) != n) or \
             (blocks is not None and len(blocks) != n):
@@ -312,8 +314,26 @@ def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp
     for i in range(n):
         arr[i] = make_matrix(params[i], grads[i], moms[i], update_outs[i] if update_outs is not None else None,
                              blocks[i] if blocks is not None else (0, 0))
+    return arr, n
+
+
+def muon_step(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp: Hparams,
+              update_outs: Optional[Sequence] = None, stream=None, blocks: Optional[Sequence] = None) -> None:
+    """One Muon step over every (param, grad, momentum) triple, on ``stream``;
+    ``blocks[i]`` = (block_rows, block_cols) of matrix i, or None for all (0, 0)."""
+    arr, n = _matrices(params, grads, moms, update_outs, blocks)
     c_hp = hp.to_c()
     st = load().muon_step(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream))
+    _check(handle, st)
+
+
+def muon_step_noalloc(handle: int, params: Sequence, grads: Sequence, moms: Sequence, hp: Hparams,
+                      update_outs: Optional[Sequence] = None, stream=None, blocks: Optional[Sequence] = None) -> None:
+    """muon_step without any device allocation: the library's static
+    per-GPU scratch holds every buffer beyond the caller's tensors."""
+    arr, n = _matrices(params, grads, moms, update_outs, blocks)
+    c_hp = hp.to_c()
+    st = load().muon_step_noalloc(handle, arr, n, ctypes.byref(c_hp), _stream_ptr(stream))
     _check(handle, st)
 
 

@@ -14,6 +14,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -396,9 +397,16 @@ muon_status append_blocks(muon_handle* h, const MatIn& m, int32_t block_rows, in
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Static geometry, workspace layout, units and tiles for one call signature.
-muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, const std::vector<int64_t>& key,
-                       hipStream_t stream, Plan** out) {
+// Host side of a plan: static geometry, workspace layout, units and tile
+// lists of one call signature (no device memory).
+struct PlanLayout {
+    std::vector<MatDesc> geom;
+    std::vector<Unit> units;
+    std::vector<Tile> lists[3][3];   // [phase: GRAM, POLY, AXPY][list kind]
+    size_t ws_bytes = 0;
+};
+
+muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, PlanLayout& L) {
     const int n = int(mats.size());
     std::vector<MatDesc> geom(n);
     std::vector<Unit> units;
@@ -549,6 +557,23 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
         }
     }
 
+    L.geom = std::move(geom);
+    L.units = std::move(units);
+    for (int l = 0; l < 3; ++l)
+        for (int lk = 0; lk < 3; ++lk) L.lists[l][lk] = std::move(lists[l][lk]);
+    L.ws_bytes = off;
+    return MUON_OK;
+}
+
+// A plan of its own for a new signature: device tables and a zero-filled
+// workspace, uploaded and waited for once.
+muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, const std::vector<int64_t>& key,
+                       hipStream_t stream, Plan** out) {
+    const int n = int(mats.size());
+    PlanLayout L;
+    muon_status st = layout_plan(h, mats, f32c, L);
+    if (st != MUON_OK) return st;
+    const size_t off = L.ws_bytes;
     if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "workspace allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
 
     std::unique_ptr<Plan> q(new (std::nothrow) Plan());
@@ -560,10 +585,10 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     bool ok = true;
     for (int l = 0; ok && l < 3; ++l)
         for (int lk = 0; ok && lk < 3; ++lk)
-            if (!lists[l][lk].empty())
-                ok = dmalloc(reinterpret_cast<void**>(&tl[l][lk].d), sizeof(Tile) * lists[l][lk].size());
-    ok = ok && dmalloc(reinterpret_cast<void**>(&q->d_units), sizeof(Unit) * units.size()) &&
-         dmalloc(reinterpret_cast<void**>(&q->d_partials), sizeof(double) * units.size()) &&
+            if (!L.lists[l][lk].empty())
+                ok = dmalloc(reinterpret_cast<void**>(&tl[l][lk].d), sizeof(Tile) * L.lists[l][lk].size());
+    ok = ok && dmalloc(reinterpret_cast<void**>(&q->d_units), sizeof(Unit) * L.units.size()) &&
+         dmalloc(reinterpret_cast<void**>(&q->d_partials), sizeof(double) * L.units.size()) &&
          dmalloc(reinterpret_cast<void**>(&q->d_norm), sizeof(NormScale) * n) &&
          dmalloc(reinterpret_cast<void**>(&q->ws), off);
     if (!ok) {
@@ -571,7 +596,7 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
         free_plan(*q);
         return fail(h, MUON_ERR_OOM, "workspace allocation of %.3f GB failed", double(off) / 1e9);
     }
-    muon_status st = alloc_staging(h, q->tabs.stage, sizeof(MatDesc) * n);
+    st = alloc_staging(h, q->tabs.stage, sizeof(MatDesc) * n);
     if (st != MUON_OK) {
         free_plan(*q);
         return st;
@@ -580,12 +605,13 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     hipError_t e = launch_fill_zero(q->ws, off, stream);
     for (int l = 0; e == hipSuccess && l < 3; ++l)
         for (int lk = 0; e == hipSuccess && lk < 3; ++lk)
-            if (!lists[l][lk].empty()) {
-                e = hipMemcpyAsync(tl[l][lk].d, lists[l][lk].data(), sizeof(Tile) * lists[l][lk].size(),
+            if (!L.lists[l][lk].empty()) {
+                e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
                                    hipMemcpyHostToDevice, stream);
-                tl[l][lk].n = int(lists[l][lk].size());
+                tl[l][lk].n = int(L.lists[l][lk].size());
             }
-    if (e == hipSuccess) e = hipMemcpyAsync(q->d_units, units.data(), sizeof(Unit) * units.size(), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(q->d_units, L.units.data(), sizeof(Unit) * L.units.size(), hipMemcpyHostToDevice, stream);
     // the host vectors die with this call: wait for the copies
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
@@ -593,8 +619,8 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
         return hip_fail(h, e, "plan upload");
     }
     q->n = n;
-    q->geom = std::move(geom);
-    q->n_units = int(units.size());
+    q->geom = std::move(L.geom);
+    q->n_units = int(L.units.size());
     q->key = key;
     Plan* raw = q.get();
     h->plans[key] = std::move(q);
@@ -614,10 +640,11 @@ hipEvent_t get_event(muon_handle* h) {
 }
 
 // `launch(ev0, ev1)` enqueues one kernel; on a profiling handle the dispatch
-// records ev0 / ev1 at its start and end.
+// records ev0 / ev1 at its start and end (unless `events` is false: the
+// no-allocation entry point creates no events).
 template <class F>
-hipError_t timed(muon_handle* h, int role, F&& launch) {
-    if (!h->profile || !((h->role_mask >> role) & 1u)) return launch(nullptr, nullptr);
+hipError_t timed(muon_handle* h, int role, F&& launch, bool events = true) {
+    if (!events || !h->profile || !((h->role_mask >> role) & 1u)) return launch(nullptr, nullptr);
     hipEvent_t a = get_event(h), b = get_event(h);
     if (!a || !b) return launch(nullptr, nullptr);
     const hipError_t e = launch(a, b);
@@ -645,16 +672,10 @@ hipError_t launch_phase_lists(int kind, const TileList (&l)[3], const MatDesc* d
     return hipSuccess;
 }
 
-muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream,
-                 Plan** used) {
-    const int n = int(mats.size());
-    const bool f32c = hp->compute == MUON_COMPUTE_FP32;
-    bool capturing = false;
-    muon_status st = capture_state(h, stream, &capturing);
-    if (st != MUON_OK) return st;
+std::vector<int64_t> signature(const std::vector<MatIn>& mats, bool f32c) {
     std::vector<int64_t> key;
-    key.reserve(2 + 5 * size_t(n));
-    key.push_back(n);
+    key.reserve(2 + 5 * mats.size());
+    key.push_back(int64_t(mats.size()));
     key.push_back(f32c);
     for (const MatIn& m : mats) {
         key.push_back(m.R);
@@ -663,23 +684,13 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
         key.push_back(m.has_param);
         key.push_back(m.has_mom);
     }
-    Plan* pp = nullptr;
-    auto it = h->plans.find(key);
-    if (it != h->plans.end()) {
-        pp = it->second.get();
-    } else {
-        if (capturing)
-            return fail(h, MUON_ERR_INVALID_ARG,
-                        "a call captured into a HIP graph must first run once outside capture with the same shapes "
-                        "and pointers (its plan and descriptor table are then resident)");
-        st = build_plan(h, mats, f32c, key, stream, &pp);
-        if (st != MUON_OK) return st;
-    }
-    Plan& plan = *pp;
+    return key;
+}
 
-    // descriptor table: static geometry + this call's pointers
-    std::vector<MatDesc> desc(plan.geom);
-    for (int i = 0; i < n; ++i) {
+// Descriptor table of one call: the plan's static geometry + the call's pointers.
+std::vector<MatDesc> call_descriptors(const std::vector<MatDesc>& geom, const std::vector<MatIn>& mats) {
+    std::vector<MatDesc> desc(geom);
+    for (size_t i = 0; i < mats.size(); ++i) {
         const MatIn& m = mats[i];
         MatDesc& d = desc[i];
         d.param = m.param;
@@ -692,20 +703,19 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
         d.ld_upd = m.ld_upd;
         d.vec_ok = (m.C % 8 == 0) && (m.ld_grad % 8 == 0) && aligned16(m.grad) &&
                    (!m.has_mom || ((m.ld_mom % 8 == 0) && aligned16(m.mom)));
-        {
-            const int64_t pe = m.dtype == MUON_BF16 ? 8 : 16;   // bytes of 4 param/grad elements
-            auto al = [](const void* q, int64_t b) { return (reinterpret_cast<uintptr_t>(q) % uintptr_t(b)) == 0; };
-            d.vec_io = (m.C % 4 == 0) && (m.ld_grad % 4 == 0) && al(m.grad, pe) &&
-                       (!m.has_param || ((m.ld_param % 4 == 0) && al(m.param, pe))) &&
-                       (!m.has_mom || ((m.ld_mom % 4 == 0) && al(m.mom, 16))) &&
-                       (!m.upd || ((m.ld_upd % 4 == 0) && al(m.upd, 16)));
-        }
+        const int64_t pe = m.dtype == MUON_BF16 ? 8 : 16;   // bytes of 4 param/grad elements
+        auto al = [](const void* q, int64_t b) { return (reinterpret_cast<uintptr_t>(q) % uintptr_t(b)) == 0; };
+        d.vec_io = (m.C % 4 == 0) && (m.ld_grad % 4 == 0) && al(m.grad, pe) &&
+                   (!m.has_param || ((m.ld_param % 4 == 0) && al(m.param, pe))) &&
+                   (!m.has_mom || ((m.ld_mom % 4 == 0) && al(m.mom, 16))) &&
+                   (!m.upd || ((m.ld_upd % 4 == 0) && al(m.upd, 16)));
     }
-    const MatDesc* d_desc = nullptr;
-    st = select_table(h, plan.tabs, desc, capturing, stream, &d_desc);
-    if (st != MUON_OK) return st;
-    if (used) *used = pp;
+    return desc;
+}
 
+// The launches of one step over a plan's device tables and workspace.
+muon_status enqueue_step(muon_handle* h, const Plan& plan, const MatDesc* d_desc, int n, const muon_hparams* hp,
+                         hipStream_t stream, bool events = true) {
     MomentumArgs ma;
     ma.ws = plan.ws;
     ma.partials = plan.d_partials;
@@ -713,11 +723,11 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
     ma.nesterov = hp->nesterov;
     hipError_t e = timed(h, K_MOMENTUM, [&](hipEvent_t e0, hipEvent_t e1) {
         return launch_momentum(plan.d_units, plan.n_units, d_desc, ma, stream, e0, e1);
-    });
+    }, events);
     if (e != hipSuccess) return hip_fail(h, e, "momentum launch");
     e = timed(h, K_FINALIZE, [&](hipEvent_t e0, hipEvent_t e1) {
         return launch_finalize_norm(d_desc, n, plan.d_partials, plan.d_norm, hp->eps, stream, e0, e1);
-    });
+    }, events);
     if (e != hipSuccess) return hip_fail(h, e, "norm launch");
 
     PhaseArgs pa;
@@ -734,13 +744,13 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
     if (hp->ns_steps == 0) {
         e = timed(h, K_DIRECT, [&](hipEvent_t e0, hipEvent_t e1) {
             return launch_direct_update(plan.d_units, plan.n_units, d_desc, pa, stream, e0, e1);
-        });
+        }, events);
         if (e != hipSuccess) return hip_fail(h, e, "update launch");
         return MUON_OK;
     }
     e = timed(h, K_RESCALE, [&](hipEvent_t e0, hipEvent_t e1) {
         return launch_rescale(plan.d_units, plan.n_units, d_desc, plan.d_norm, plan.ws, stream, e0, e1);
-    });
+    }, events);
     if (e != hipSuccess) return hip_fail(h, e, "rescale launch");
     for (int it = 1; it <= hp->ns_steps; ++it) {
         pa.iter = it;
@@ -751,19 +761,155 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
         }
         e = timed(h, K_GRAM, [&](hipEvent_t e0, hipEvent_t e1) {
             return launch_phase_lists(PH_GRAM, plan.gram, d_desc, pa, stream, e0, e1);
-        });
+        }, events);
         if (e != hipSuccess) return hip_fail(h, e, "gram launch");
         e = timed(h, K_POLY, [&](hipEvent_t e0, hipEvent_t e1) {
             return launch_phase_lists(PH_POLY, plan.poly, d_desc, pa, stream, e0, e1);
-        });
+        }, events);
         if (e != hipSuccess) return hip_fail(h, e, "poly launch");
         const bool last = it == hp->ns_steps;
         e = timed(h, last ? K_AXPY_LAST : K_AXPY, [&](hipEvent_t e0, hipEvent_t e1) {
             return launch_phase_lists(last ? PH_AXPY_LAST : PH_AXPY, plan.axpy, d_desc, pa, stream, e0, e1);
-        });
+        }, events);
         if (e != hipSuccess) return hip_fail(h, e, "axpy launch");
     }
     return MUON_OK;
+}
+
+muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream,
+                 Plan** used) {
+    const int n = int(mats.size());
+    const bool f32c = hp->compute == MUON_COMPUTE_FP32;
+    bool capturing = false;
+    muon_status st = capture_state(h, stream, &capturing);
+    if (st != MUON_OK) return st;
+    const std::vector<int64_t> key = signature(mats, f32c);
+    Plan* pp = nullptr;
+    auto it = h->plans.find(key);
+    if (it != h->plans.end()) {
+        pp = it->second.get();
+    } else {
+        if (capturing)
+            return fail(h, MUON_ERR_INVALID_ARG,
+                        "a call captured into a HIP graph must first run once outside capture with the same shapes "
+                        "and pointers (its plan and descriptor table are then resident)");
+        st = build_plan(h, mats, f32c, key, stream, &pp);
+        if (st != MUON_OK) return st;
+    }
+    Plan& plan = *pp;
+    const std::vector<MatDesc> desc = call_descriptors(plan.geom, mats);
+    const MatDesc* d_desc = nullptr;
+    st = select_table(h, plan.tabs, desc, capturing, stream, &d_desc);
+    if (st != MUON_OK) return st;
+    if (used) *used = pp;
+    return enqueue_step(h, plan, d_desc, n, hp, stream);
+}
+
+// ---- the no-allocation variant: everything in the device's static scratch ----
+
+// What one device's scratch holds: the signature whose layout (zero-filled
+// workspace, tile lists, units) was written last and the descriptor table
+// written last.  Guarded by `mu`; the scratch itself is shared by every call
+// on the device, so calls that overlap on one GPU race.
+struct StaticDevice {
+    std::mutex mu;
+    std::vector<int64_t> key;
+    std::vector<MatDesc> desc;
+    bool layout_valid = false, desc_valid = false;
+};
+StaticDevice g_static[kMaxStaticDevices];
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream) {
+    const int n = int(mats.size());
+    const bool f32c = hp->compute == MUON_COMPUTE_FP32;
+    if (h->device < 0 || h->device >= kMaxStaticDevices)
+        return fail(h, MUON_ERR_INVALID_ARG, "device %d: the static scratch serves devices 0..%d", h->device,
+                    kMaxStaticDevices - 1);
+    const std::vector<int64_t> key = signature(mats, f32c);
+    PlanLayout L;
+    muon_status st = layout_plan(h, mats, f32c, L);
+    if (st != MUON_OK) return st;
+    // scratch layout: workspace | 9 tile lists | units | partials | norms | descriptors
+    size_t off = align256(L.ws_bytes);
+    size_t list_off[3][3];
+    for (int l = 0; l < 3; ++l)
+        for (int lk = 0; lk < 3; ++lk) {
+            list_off[l][lk] = off;
+            off = align256(off + sizeof(Tile) * L.lists[l][lk].size());
+        }
+    const size_t units_off = off;
+    off = align256(off + sizeof(Unit) * L.units.size());
+    const size_t partials_off = off;
+    off = align256(off + sizeof(double) * L.units.size());
+    const size_t norm_off = off;
+    off = align256(off + sizeof(NormScale) * size_t(n));
+    const size_t desc_off = off;
+    off = align256(off + sizeof(MatDesc) * size_t(n));
+    if (off > kStaticScratchBytes)
+        return fail(h, MUON_ERR_INVALID_ARG,
+                    "this call needs %.1f MiB of scratch (workspace %.1f MiB); the static scratch holds %.0f MiB",
+                    double(off) / (1 << 20), double(L.ws_bytes) / (1 << 20), double(kStaticScratchBytes) / (1 << 20));
+    char* base = nullptr;
+    hipError_t e = static_scratch_base(h->device, &base);
+    if (e != hipSuccess) return hip_fail(h, e, "static scratch address");
+
+    Plan plan;   // views into the scratch: owns no device memory
+    TileList* tl[3] = {plan.gram, plan.poly, plan.axpy};
+    for (int l = 0; l < 3; ++l)
+        for (int lk = 0; lk < 3; ++lk) {
+            tl[l][lk].d = reinterpret_cast<Tile*>(base + list_off[l][lk]);
+            tl[l][lk].n = int(L.lists[l][lk].size());
+        }
+    plan.d_units = reinterpret_cast<Unit*>(base + units_off);
+    plan.n_units = int(L.units.size());
+    plan.d_partials = reinterpret_cast<double*>(base + partials_off);
+    plan.d_norm = reinterpret_cast<NormScale*>(base + norm_off);
+    plan.ws = base;
+    plan.ws_bytes = L.ws_bytes;
+    MatDesc* d_desc = reinterpret_cast<MatDesc*>(base + desc_off);
+    const std::vector<MatDesc> desc = call_descriptors(L.geom, mats);
+
+    StaticDevice& sd = g_static[h->device];
+    std::lock_guard<std::mutex> lock(sd.mu);
+    // The scratch keeps the last call's contents.  A new signature moves the
+    // layout: clear the workspace (its padding must read as zeros) and write
+    // the tile lists and units; a new descriptor table is written too.  Each
+    // copy reads host memory that dies with this call, so the stream is waited
+    // for before returning from such a call.
+    bool wait = false;
+    if (!sd.layout_valid || sd.key != key) {
+        sd.layout_valid = false;
+        sd.desc_valid = false;
+        e = launch_fill_zero(base, L.ws_bytes, stream);
+        for (int l = 0; e == hipSuccess && l < 3; ++l)
+            for (int lk = 0; e == hipSuccess && lk < 3; ++lk)
+                if (!L.lists[l][lk].empty())
+                    e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
+                                       hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(plan.d_units, L.units.data(), sizeof(Unit) * L.units.size(), hipMemcpyHostToDevice,
+                               stream);
+        if (e != hipSuccess) return hip_fail(h, e, "static scratch layout upload");
+        wait = true;
+    }
+    if (!sd.desc_valid || sd.desc.size() != desc.size() ||
+        std::memcmp(sd.desc.data(), desc.data(), sizeof(MatDesc) * desc.size()) != 0) {
+        sd.desc_valid = false;
+        e = hipMemcpyAsync(d_desc, desc.data(), sizeof(MatDesc) * desc.size(), hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(h, e, "static scratch descriptor upload");
+        wait = true;
+    }
+    if (wait) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(h, e, "static scratch upload wait");
+        sd.key = key;
+        sd.layout_valid = true;
+        sd.desc = desc;
+        sd.desc_valid = true;
+    }
+    return enqueue_step(h, plan, d_desc, n, hp, stream, false);
 }
 
 }  // namespace
@@ -822,6 +968,32 @@ muon_status muon_step(muon_handle* h, const muon_matrix* mats, int32_t n_mats, c
         h->last_step_n = int(in.size());
     }
     return st;
+}
+
+muon_status muon_step_noalloc(muon_handle* h, const muon_matrix* mats, int32_t n_mats, const muon_hparams* hp,
+                              void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    h->err.clear();
+    if (n_mats < 0) return fail(h, MUON_ERR_INVALID_ARG, "n_mats %d < 0", n_mats);
+    if (n_mats == 0) return MUON_OK;
+    if (!mats) return fail(h, MUON_ERR_INVALID_ARG, "mats is NULL");
+    muon_status st = validate_hp(h, hp);
+    if (st != MUON_OK) return st;
+    std::vector<MatIn> in;
+    in.reserve(size_t(n_mats));
+    for (int i = 0; i < n_mats; ++i) {
+        const muon_matrix& m = mats[i];
+        if (m.reserved != 0) return fail(h, MUON_ERR_INVALID_ARG, "matrix %d: reserved field must be 0", i);
+        const MatIn whole{m.param, m.grad, m.momentum, m.update_out, m.rows, m.cols, m.ld_param,
+                          m.ld_grad, m.ld_mom, m.update_out ? m.ld_update : 0, m.dtype, true, true};
+        st = validate_mat(h, whole, i);
+        if (st != MUON_OK) return st;
+        st = append_blocks(h, whole, m.block_rows, m.block_cols, i, in);
+        if (st != MUON_OK) return st;
+    }
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(h, MUON_ERR_NO_DEVICE, "cannot select device %d", h->device);
+    return run_static(h, in, hp, static_cast<hipStream_t>(stream));
 }
 
 muon_status muon_orthogonalize(muon_handle* h, const void* in, float* out, int64_t rows, int64_t cols, int64_t ld_in,

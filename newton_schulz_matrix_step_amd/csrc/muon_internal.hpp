@@ -137,6 +137,14 @@ struct AdamArgs {
 hipError_t launch_adamw(const AdamChunk* chunks, int n_chunks, const AdamDesc* tensors, AdamArgs a, hipStream_t s,
                         hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
+// ---- static scratch of the no-allocation entry point (muon_static.hip) ----
+// A file-scope device array of this many bytes per GPU, held until the
+// process ends; its device address is looked up once per device.
+constexpr size_t kStaticScratchBytes = size_t(256) << 20;
+constexpr int kMaxStaticDevices = 64;
+// Device address of the scratch on `device` (which must be current).
+hipError_t static_scratch_base(int device, char** base);
+
 // Tile edge of the Newton-Schulz GEMMs (both modes use 128 x 128 tiles).
 constexpr int kTileF32 = 128;
 constexpr int kTileBf16 = 128;

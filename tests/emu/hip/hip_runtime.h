@@ -23,6 +23,8 @@
 #define __launch_bounds__(...)
 #define __shared__ static
 #define LDS_AS
+#define __align__(n) __attribute__((aligned(n)))
+#define HIP_SYMBOL(x) (&(x))
 
 struct dim3 {
     unsigned x, y, z;
@@ -58,6 +60,11 @@ inline hipError_t hipEventSynchronize(hipEvent_t) { return hipSuccess; }
 inline hipError_t hipEventDestroy(hipEvent_t) { return hipSuccess; }
 inline hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) { *ms = 0; return hipSuccess; }
 inline hipError_t hipGetLastError() { return hipSuccess; }
+enum { hipErrorInvalidDevice = 101 };
+template <class T> inline hipError_t hipGetSymbolAddress(void** p, T sym) {
+    *p = (void*)sym;
+    return hipSuccess;
+}
 enum hipStreamCaptureStatus { hipStreamCaptureStatusNone = 0, hipStreamCaptureStatusActive = 1 };
 inline hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* s) {
     *s = hipStreamCaptureStatusNone;

@@ -30,6 +30,9 @@ CASES = [
     ("384x96,130x60", 2, 0, 65),
     ("300x100,100x300,129x515,515x129,64x64,1x17,17x1,200x199", 2, 0, 0, 0, 0, 1e15),
     ("300x100,100x300,129x515,33x64", 2, 1, 0, 5, 1, 1e15),
+    # the no-allocation entry point: static scratch, a call then a smaller one
+    ("300x100,100x300,129x515,515x129,64x64,1x17,17x1", 2, 0, 0, 0, 0, 0, 1),
+    ("300x100,33x64", 2, 1, 0, 5, 1, 1e15, 1),
 ]
 
 
@@ -46,7 +49,7 @@ def _build(tmp_path_factory, name, extra):
              f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-Wno-unused-value", *extra]
     objs = []
     for src, lang in (("muon_kernels.hip", ["-x", "c++"]), ("adamw_kernels.hip", ["-x", "c++"]),
-                      ("muon_api.cpp", [])):
+                      ("muon_static.hip", ["-x", "c++"]), ("muon_api.cpp", [])):
         obj = str(out / (src + ".o"))
         subprocess.run([CXX, *flags, *lang, os.path.join(CSRC, src), "-c", "-o", obj], check=True)
         objs.append(obj)
