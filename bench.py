@@ -54,17 +54,28 @@ def block_shapes(wl, i):
 
 
 def algorithmic_work(wl):
-    """Per-launch algorithmic flops of each Newton-Schulz role and bytes of the
-    momentum pass, summed over the workload's matrices.
+    """Per-launch algorithmic flops and bytes of each Newton-Schulz role and
+    bytes of the momentum pass, summed over the workload's matrices.
 
-    GRAM: m(m+1) n (the m(m+1)/2 distinct entries of X X^T, 2n flops each);
-    POLY: m^2 (m+1) (distinct entries of A A); AXPY: 2 m^2 n.
+    Flops: GRAM m(m+1) n (the m(m+1)/2 distinct entries of X X^T, 2n flops
+    each); POLY m^2 (m+1) (distinct entries of A A); AXPY 2 m^2 n.
+    Bytes (each input read once, each output written once, as the kernels
+    store them; e = 2 bytes per bf16 operand element and a 1-byte remainder of
+    the master X, e = 4 and no remainder for float32 entries):
+      GRAM  read X (e RC), write A (e m^2);  POLY read A, write B (2 e m^2);
+      AXPY, first iteration: read the copy of u (e RC), m' (4 RC), with
+        Nesterov g too, and B (e m^2); write X' (copy + remainder);
+      AXPY, middle iterations: read and write X (copy + remainder), read B;
+      AXPY, last iteration: read X and B, read and write W.
+    ``ns_axpy`` averages the first and the middle iterations (the launches
+    that role covers); ``ns_axpy_update`` is the last one.
     Momentum pass: read g (2 B bf16 / 4 B fp32) and m (4 B), write m' (4 B)
     and the operand copy of u (2 B bf16 / 4 B fp32).
     """
     gb = 2 if wl.storage == "bf16" else 4
     ub = 2 if wl.compute == "bf16" else 4
     gram = poly = axpy = dense = 0
+    b_gram = b_poly = b_first = b_mid = b_last = 0
     elems = 0
     for i, s in enumerate(wl.mats):
         for (r, c) in block_shapes(wl, i):
@@ -73,9 +84,20 @@ def algorithmic_work(wl):
             poly += m * m * (m + 1)
             axpy += 2 * m * m * n
             dense += 4 * m * m * n + 2 * m ** 3
+            f32 = wl.compute == "fp32" or m <= 64
+            e, lo = (4, 0) if f32 else (2, 1)
+            rc = r * c
+            b_gram += e * rc + e * m * m
+            b_poly += 2 * e * m * m
+            b_first += e * rc + 4 * rc + (gb * rc if wl.nesterov else 0) + e * m * m + (e + lo) * rc
+            b_mid += 2 * (e + lo) * rc + e * m * m
+            b_last += (e + lo) * rc + e * m * m + 2 * gb * rc
         elems += s.rows * s.cols
+    n_axpy = max(wl.ns_steps - 1, 1)
+    b_axpy = (b_first + max(wl.ns_steps - 2, 0) * b_mid) / n_axpy
     return {
         "flops": {"ns_gram": gram, "ns_poly": poly, "ns_axpy": axpy, "ns_axpy_update": axpy},
+        "bytes": {"ns_gram": b_gram, "ns_poly": b_poly, "ns_axpy": b_axpy, "ns_axpy_update": b_last},
         "ns_flops_per_step": wl.ns_steps * (gram + poly + axpy),
         "ns_dense_flops_per_step": wl.ns_steps * dense,   # the pages' convention, 4 m^2 n + 2 m^3 an iteration
         "momentum_bytes": elems * (gb + 4 + 4 + ub),
@@ -162,6 +184,46 @@ def copy_calibration(mib: int, reps: int = 5):
                       "read_plus_write_gbs": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def yardstick(wl, reps: int = 20):
+    """The library GEMM as a yardstick: torch.matmul (hipBLASLt, bf16, dense)
+    on each distinct product shape of one Newton-Schulz iteration of the
+    workload (X X^T as m x n by n x m, A A as m x m by m x m, B X as m x m by
+    m x n), one product per shape, timed with events; dense flops 2 m k n."""
+    import torch
+    dev = torch.device("cuda:0")
+    shapes = sorted({(min(r, c), max(r, c)) for i in range(len(wl.mats)) for (r, c) in block_shapes(wl, i)})
+    out = []
+    for m, n in shapes:
+        for what, (a, b) in (("X X^T", ((m, n), (n, m))), ("A A", ((m, m), (m, m))), ("B X", ((m, m), (m, n)))):
+            x = torch.randn(*a, device=dev, dtype=torch.bfloat16)
+            y = torch.randn(*b, device=dev, dtype=torch.bfloat16)
+            for _ in range(3):
+                torch.matmul(x, y)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.matmul(x, y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            fl = 2.0 * a[0] * a[1] * b[1]
+            out.append({"product": what, "m": a[0], "k": a[1], "n": b[1], "us": round(ms * 1e3, 2),
+                        "tflops": round(fl / (ms * 1e-3) / 1e12, 1)})
+    return out
+
+
 def cpu_baseline(wl, grads_host, budget_s: float):
     """The oracle, as it stands, on the host cores: whole matrices of the first
     step until ``budget_s`` seconds of work, extrapolated to one full step."""
@@ -214,6 +276,7 @@ def cpu_baseline(wl, grads_host, budget_s: float):
         "value": 1.0 / est,
         "unit": "steps/s",
         "cores": int(cores),
+        "cpu_model": host_cpu_model(),
         "kind": "oracle",
         "sample": what + "; steps/s = Newton-Schulz flops of one step / flops done per second",
     }
@@ -341,7 +404,7 @@ def adamw_bench(args):
             done += wl.tensors[k].numel
             k += 1
         out["cpu_baseline"] = {"value": round(1.0 / (t_used * wl.elements / max(done, 1)), 4), "unit": "steps/s",
-                               "cores": int(cores), "kind": "oracle",
+                               "cores": int(cores), "cpu_model": host_cpu_model(), "kind": "oracle",
                                "sample": f"{k} of {n} tensors of step 1 ({done}/{wl.elements} elements), "
                                          f"{t_used:.1f} s of float64 NumPy, extrapolated by elements"}
     print(json.dumps(out), flush=True)
@@ -358,6 +421,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="only time torch.matmul (hipBLASLt) on the workload's product shapes and exit")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
@@ -376,6 +441,12 @@ def main():
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+
+    if args.yardstick:
+        from muon_synth import workload as _wl
+        print(json.dumps({"yardstick": "torch.matmul bf16", "workload": args.workload,
+                          "products": yardstick(_wl(args.workload))}), flush=True)
         return
 
     from muon_synth import ADAMW_WORKLOADS
@@ -509,6 +580,7 @@ def main():
         ent = {"launches": launches, "avg_us": round(avg_us, 2), "ms_per_step": round(total_ms / args.steps, 4)}
         if name in work["flops"]:
             ent["tflops"] = round(work["flops"][name] / (avg_us * 1e-6) / 1e12, 2)
+            ent["gbs"] = round(work["bytes"][name] / (avg_us * 1e-6) / 1e9, 1)
         if name == "momentum_norm":
             ent["gbs"] = round(work["momentum_bytes"] / (avg_us * 1e-6) / 1e9, 1)
         kernels[name] = ent
@@ -517,16 +589,30 @@ def main():
     peak = PEAK_BF16_TFLOPS if wl.compute == "bf16" else PEAK_FP32_TFLOPS
 
     dom_avg_s = dom_stats[1] * 1e-3 / dom_stats[0]
-    achieved = work["flops"][dom] / dom_avg_s / 1e12
-    roofline = {
-        "kernel": f"ns_gemm_bf16 ({dom})" if wl.compute == "bf16" else f"ns_gemm_kernel ({dom})",
-        "bound": "mfma",
-        "achieved": round(achieved, 2),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
+    # the kernel's roofline: algorithmic flops against the MFMA peak and
+    # algorithmic bytes against HBM; the one that takes longer at its peak
+    # bounds the kernel and is the one reported
+    flops, nbytes = work["flops"][dom], work["bytes"][dom]
+    t_mfma, t_hbm = flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+    mfma_frac = t_mfma / dom_avg_s
+    hbm_frac = t_hbm / dom_avg_s
+    kname = f"ns_gemm_bf16 ({dom})" if wl.compute == "bf16" else f"ns_gemm_kernel ({dom})"
+    if t_mfma >= t_hbm:
+        roofline = {"kernel": kname, "bound": "mfma", "achieved": round(flops / dom_avg_s / 1e12, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
+    else:
+        roofline = {"kernel": kname, "bound": "hbm", "achieved": round(nbytes / dom_avg_s / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm_frac, 4)}
+    roofline.update({
         "traffic": None,
-    }
+        "algorithmic_flops": int(flops),
+        "algorithmic_bytes": int(nbytes),
+        "flop_per_byte": round(flops / nbytes, 1),
+        "ridge_flop_per_byte": round(peak * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+        "mfma_frac": round(mfma_frac, 4),
+        "hbm_frac": round(hbm_frac, 4),
+        "avg_launch_us": round(dom_avg_s * 1e6, 2),
+    })
     tr = recorded_traffic(dom, wl.name)
     if tr is not None:
         roofline["traffic"] = round(tr["fetch"] + tr["write"])

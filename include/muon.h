@@ -73,6 +73,10 @@ typedef enum muon_compute {
 /* init flags */
 #define MUON_INIT_PROFILE     0x1u   /* time kernel launches with HIP events (all roles, or see below) */
 #define MUON_INIT_FAIL_ALLOC  0x2u   /* test hook: every workspace allocation fails (MUON_ERR_OOM) */
+#define MUON_INIT_DEBUG       0x4u   /* debug checks: a guard band of a fixed pattern after every workspace
+                                        buffer of muon_step's plans, checked after every step (which then
+                                        waits for its stream); an overwritten band fails the call with
+                                        MUON_ERR_HIP and the count of damaged words in muon_last_error */
 
 /* Kernel roles, as named in muon_kernel_stats.name. */
 typedef enum muon_role {

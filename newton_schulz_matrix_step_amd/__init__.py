@@ -18,6 +18,7 @@ from ._abi import (  # noqa: F401
     MUON_ERR_NO_DEVICE,
     MUON_ERR_OOM,
     MUON_F32,
+    MUON_INIT_DEBUG,
     MUON_INIT_FAIL_ALLOC,
     MUON_INIT_PROFILE,
     MUON_OK,

@@ -32,6 +32,7 @@ MUON_COMPUTE_FP32 = 1
 
 MUON_INIT_PROFILE = 0x1
 MUON_INIT_FAIL_ALLOC = 0x2
+MUON_INIT_DEBUG = 0x4
 
 # kernel roles (muon_role), named as in muon_kernel_stats
 ROLE_NAMES = ("momentum_norm", "norm_finalize", "ns_gram", "ns_poly", "ns_axpy", "ns_axpy_update",

@@ -42,9 +42,10 @@ enum KernelRole {
     K_RESCALE,
     K_NROLES
 };
-static_assert(K_MOMENTUM == MUON_ROLE_MOMENTUM && K_GRAM == MUON_ROLE_GRAM && K_AXPY == MUON_ROLE_AXPY &&
-                  K_AXPY_LAST == MUON_ROLE_AXPY_UPDATE && K_ADAMW == MUON_ROLE_ADAMW &&
-                  K_RESCALE == MUON_ROLE_RESCALE && K_NROLES == 10,
+static_assert(int(K_MOMENTUM) == int(MUON_ROLE_MOMENTUM) && int(K_GRAM) == int(MUON_ROLE_GRAM) &&
+                  int(K_AXPY) == int(MUON_ROLE_AXPY) && int(K_AXPY_LAST) == int(MUON_ROLE_AXPY_UPDATE) &&
+                  int(K_ADAMW) == int(MUON_ROLE_ADAMW) && int(K_RESCALE) == int(MUON_ROLE_RESCALE) &&
+                  K_NROLES == 10,
               "kernel roles follow muon_role");
 const char* const kRoleNames[K_NROLES] = {"momentum_norm", "norm_finalize", "ns_gram", "ns_poly",
                                           "ns_axpy", "ns_axpy_update", "direct_update", "fill_zero",
@@ -58,20 +59,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxEntries = 65536;   // plan entries (matrices or blocks) per muon_step call
 #ifndef MUON_UNIT_ELEMS
-#define MUON_UNIT_ELEMS 16384
+#define MUON_UNIT_ELEMS 8192
 #endif
 constexpr int kUnitElems = MUON_UNIT_ELEMS;  // momentum-pass elements per workgroup (target)
-// 256-wide tiles: bf16-iteration entries with min(R, C) >= kWideMinM are
-// padded to 256 and run the phases in kWidePhases (bit 0 GRAM, 1 POLY, 2 AXPY)
-// on 256 x 256 tiles, the rest on 128 x 128.
-#ifndef MUON_WIDE_MIN_M
-#define MUON_WIDE_MIN_M (1 << 30)
-#endif
-#ifndef MUON_WIDE_PHASES
-#define MUON_WIDE_PHASES 7
-#endif
-constexpr int kWideMinM = MUON_WIDE_MIN_M;
-constexpr int kWidePhases = MUON_WIDE_PHASES;
+
 // Tile rows per item of the tile lists (see build_list): GRAM / POLY items of
 // 8 rows; an AXPY output of at most 8 tile rows is one item, taller ones go in
 // items of 4 rows (8 measured slower there).
@@ -120,15 +111,17 @@ struct Plan {
     std::vector<int64_t> key;
     int n = 0;
     std::vector<MatDesc> geom;     // static part of every descriptor
-    // per phase, one list per kernel: [0] bf16 entries on 128 x 128 tiles,
-    // [1] float32 entries (128 x 128), [2] bf16 entries on 256 x 256 tiles
-    TileList gram[3], poly[3], axpy[3];
+    // per phase, one list per kernel: [0] bf16-iteration entries, [1] float32 entries
+    TileList gram[2], poly[2], axpy[2];
     Unit* d_units = nullptr;
     int n_units = 0;
     double* d_partials = nullptr;
     NormScale* d_norm = nullptr;
     char* ws = nullptr;
     size_t ws_bytes = 0;
+    int64_t* d_guards = nullptr;   // debug handles: guard band offsets and the check's counter
+    int n_guards = 0;
+    uint32_t* d_guard_bad = nullptr;
     TableSet<MatDesc> tabs;
 };
 
@@ -211,7 +204,7 @@ void free_tables(TableSet<D>& ts) {
 }
 
 void free_plan(Plan& p) {
-    for (int m = 0; m < 3; ++m) {
+    for (int m = 0; m < 2; ++m) {
         (void)hipFree(p.gram[m].d);
         (void)hipFree(p.poly[m].d);
         (void)hipFree(p.axpy[m].d);
@@ -220,6 +213,8 @@ void free_plan(Plan& p) {
     (void)hipFree(p.d_partials);
     (void)hipFree(p.d_norm);
     (void)hipFree(p.ws);
+    (void)hipFree(p.d_guards);
+    (void)hipFree(p.d_guard_bad);
     free_tables(p.tabs);
     p = Plan();
 }
@@ -402,21 +397,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct PlanLayout {
     std::vector<MatDesc> geom;
     std::vector<Unit> units;
-    std::vector<Tile> lists[3][3];   // [phase: GRAM, POLY, AXPY][list kind]
+    std::vector<Tile> lists[3][2];   // [phase: GRAM, POLY, AXPY][0 bf16 entries, 1 float32 entries]
+    std::vector<int64_t> guards;     // debug handles: workspace offsets of the guard bands
     size_t ws_bytes = 0;
 };
 
-muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, PlanLayout& L) {
+muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c, PlanLayout& L,
+                        bool guard_bands = false) {
     const int n = int(mats.size());
     std::vector<MatDesc> geom(n);
     std::vector<Unit> units;
     size_t off = 0;
+    // each workspace buffer 256-byte aligned; on a debug handle followed by a
+    // guard band that no kernel may write
     auto take = [&](int64_t bytes) {
         const size_t o = off;
         off += size_t(round_up(bytes, 256));
+        if (guard_bands) {
+            L.guards.push_back(int64_t(off));
+            off += kGuardBytes;
+        }
         return int64_t(o);
     };
-    std::vector<char> wide(n, 0);   // entry padded to 256 (some phases on 256 x 256 tiles)
     for (int i = 0; i < n; ++i) {
         const MatIn& m = mats[i];
         MatDesc d;
@@ -427,12 +429,10 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         d.m = int32_t(std::min(m.R, m.C));
         d.n = int32_t(std::max(m.R, m.C));
         d.f32 = f32c || d.m <= kSmallM;
-        wide[i] = !d.f32 && d.m >= kWideMinM && kWidePhases != 0;
-        const int64_t pad = wide[i] ? 256 : kPad;
-        d.Rp = int32_t(round_up(m.R, pad));
-        d.Cp = int32_t(round_up(m.C, pad));
-        d.mp = int32_t(round_up(d.m, pad));
-        d.np = int32_t(round_up(d.n, pad));
+        d.Rp = int32_t(round_up(m.R, kPad));
+        d.Cp = int32_t(round_up(m.C, kPad));
+        d.mp = int32_t(round_up(d.m, kPad));
+        d.np = int32_t(round_up(d.n, kPad));
         d.io_dtype = m.dtype;
         d.has_param = m.has_param;
         d.has_mom = m.has_mom;
@@ -453,19 +453,17 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         d.nunits = int32_t(units.size()) - d.unit0;
         geom[i] = d;
     }
-    // Newton-Schulz tile edges: 128 x 128 (two workgroups share a CU, so one
-    // tile's epilogue overlaps another's main loop; AXPY tiles of this size
-    // keep their quadrant of X from the operand stream) and, for the entries
-    // and phases the wide-tile policy above selects, 256 x 256 (one workgroup
-    // per CU, half the operand traffic and half the LDS reads per flop).
-    static_assert(kTileBf16 == kTileF32 && kTileBf16 == 128, "128 x 128 base tiles in both modes");
-    // list kind of entry i in a phase: 0 bf16 on 128 tiles, 1 float32, 2 bf16 on 256 tiles
-    auto list_kind = [&](int i, int kind) {
-        if (geom[i].f32) return 1;
-        const int bit = kind == PH_GRAM ? 1 : (kind == PH_POLY ? 2 : 4);
-        return (wide[i] && (kWidePhases & bit)) ? 2 : 0;
-    };
-    // Tile lists, one per phase and per kernel (bf16 128 / float32 / bf16 256
+    // Newton-Schulz tile edge: 128 x 128 for every phase and both modes.  Two
+    // workgroups share a CU, so one tile's epilogue overlaps another's main
+    // loop; AXPY tiles of this size also keep their quadrant of X from the
+    // operand stream.  256-wide tiles (one workgroup of four 128 x 128 waves
+    // per CU, half the operand traffic and LDS reads per flop, software
+    // pipelined) measured no faster on any workload and slower on most.
+    constexpr int T = kTileBf16;
+    static_assert(kTileBf16 == kTileF32, "one tile edge for both modes");
+    // list of entry i: 0 bf16 iteration, 1 float32 iteration
+    auto list_kind = [&](int i) { return geom[i].f32 ? 1 : 0; };
+    // Tile lists, one per phase and per iteration precision (bf16 and float32
     // entries run different kernels).  Workgroup b runs on XCD b % 8, and each
     // XCD has its own L2, so every list is 8 chunks, one per XCD: chunk x
     // holds the tiles XCD x runs, in dispatch order.  Tiles come in items (one
@@ -479,7 +477,6 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
     // tiles differently, so each gets its own list.
     auto build_list = [&](int kind, int lk, std::vector<Tile>& out) {
         const bool sym = kind != PH_AXPY;
-        const int T = lk == 2 ? 256 : 128;
         struct Item {
             int mat, a0;
             int64_t w;
@@ -496,7 +493,7 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         };
         auto item_rows = [&](int tm) { return sym ? kItemRowsSym : (tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy); };
         for (int i = 0; i < n; ++i) {
-            if (list_kind(i, kind) != lk) continue;
+            if (list_kind(i) != lk) continue;
             int tm, tn;
             dims(geom[i], tm, tn);
             const int IR = item_rows(tm);
@@ -533,15 +530,14 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         out.assign(8 * chunk, Tile{-1, 0, 0, 0});
         for (int x = 0; x < 8; ++x) std::copy(bins[x].begin(), bins[x].end(), out.begin() + x * chunk);
     };
-    std::vector<Tile> lists[3][3];
-    for (int lk = 0; lk < 3; ++lk) {
+    std::vector<Tile> lists[3][2];
+    for (int lk = 0; lk < 2; ++lk) {
         build_list(PH_GRAM, lk, lists[0][lk]);
         build_list(PH_POLY, lk, lists[1][lk]);
         build_list(PH_AXPY, lk, lists[2][lk]);
     }
     // every tile's operand panels must lie inside the padded workspace buffers
-    for (int lk = 0; lk < 3; ++lk) {
-        const int T = lk == 2 ? 256 : 128;
+    for (int lk = 0; lk < 2; ++lk) {
         for (int l = 0; l < 2; ++l)
             for (const Tile& t : lists[l][lk]) {
                 if (t.mat < 0) continue;
@@ -560,7 +556,7 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
     L.geom = std::move(geom);
     L.units = std::move(units);
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 3; ++lk) L.lists[l][lk] = std::move(lists[l][lk]);
+        for (int lk = 0; lk < 2; ++lk) L.lists[l][lk] = std::move(lists[l][lk]);
     L.ws_bytes = off;
     return MUON_OK;
 }
@@ -571,7 +567,8 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
                        hipStream_t stream, Plan** out) {
     const int n = int(mats.size());
     PlanLayout L;
-    muon_status st = layout_plan(h, mats, f32c, L);
+    const bool debug = (h->flags & MUON_INIT_DEBUG) != 0;
+    muon_status st = layout_plan(h, mats, f32c, L, debug);
     if (st != MUON_OK) return st;
     const size_t off = L.ws_bytes;
     if (h->flags & MUON_INIT_FAIL_ALLOC) return fail(h, MUON_ERR_OOM, "workspace allocation failed (forced by MUON_INIT_FAIL_ALLOC)");
@@ -584,13 +581,15 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     TileList* tl[3] = {q->gram, q->poly, q->axpy};
     bool ok = true;
     for (int l = 0; ok && l < 3; ++l)
-        for (int lk = 0; ok && lk < 3; ++lk)
+        for (int lk = 0; ok && lk < 2; ++lk)
             if (!L.lists[l][lk].empty())
                 ok = dmalloc(reinterpret_cast<void**>(&tl[l][lk].d), sizeof(Tile) * L.lists[l][lk].size());
     ok = ok && dmalloc(reinterpret_cast<void**>(&q->d_units), sizeof(Unit) * L.units.size()) &&
          dmalloc(reinterpret_cast<void**>(&q->d_partials), sizeof(double) * L.units.size()) &&
          dmalloc(reinterpret_cast<void**>(&q->d_norm), sizeof(NormScale) * n) &&
-         dmalloc(reinterpret_cast<void**>(&q->ws), off);
+         dmalloc(reinterpret_cast<void**>(&q->ws), off) &&
+         (!debug || (dmalloc(reinterpret_cast<void**>(&q->d_guards), sizeof(int64_t) * L.guards.size()) &&
+                     dmalloc(reinterpret_cast<void**>(&q->d_guard_bad), 16)));
     if (!ok) {
         (void)hipGetLastError();
         free_plan(*q);
@@ -604,7 +603,7 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     q->ws_bytes = off;
     hipError_t e = launch_fill_zero(q->ws, off, stream);
     for (int l = 0; e == hipSuccess && l < 3; ++l)
-        for (int lk = 0; e == hipSuccess && lk < 3; ++lk)
+        for (int lk = 0; e == hipSuccess && lk < 2; ++lk)
             if (!L.lists[l][lk].empty()) {
                 e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
                                    hipMemcpyHostToDevice, stream);
@@ -612,6 +611,12 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
             }
     if (e == hipSuccess)
         e = hipMemcpyAsync(q->d_units, L.units.data(), sizeof(Unit) * L.units.size(), hipMemcpyHostToDevice, stream);
+    if (debug && e == hipSuccess && !L.guards.empty()) {
+        e = hipMemcpyAsync(q->d_guards, L.guards.data(), sizeof(int64_t) * L.guards.size(), hipMemcpyHostToDevice,
+                           stream);
+        q->n_guards = int(L.guards.size());
+        if (e == hipSuccess) e = launch_guards(q->ws, q->d_guards, q->n_guards, nullptr, stream);
+    }
     // the host vectors die with this call: wait for the copies
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     if (e != hipSuccess) {
@@ -652,20 +657,15 @@ hipError_t timed(muon_handle* h, int role, F&& launch, bool events = true) {
     return e;
 }
 
-// One phase over its tile lists (bf16 entries on 128 tiles, float32 entries,
-// bf16 entries on 256 tiles); on a profiling handle the phase is timed as one,
-// from the first launch's start to the last one's end.
-hipError_t launch_phase_lists(int kind, const TileList (&l)[3], const MatDesc* desc, const PhaseArgs& pa,
+// One phase over its tile lists (bf16 entries, then float32 entries); on a
+// profiling handle the phase is timed as one, from the first launch's start
+// to the last one's end.
+hipError_t launch_phase_lists(int kind, const TileList (&l)[2], const MatDesc* desc, const PhaseArgs& pa,
                               hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-    int first = -1, last = -1;
-    for (int lk = 0; lk < 3; ++lk)
-        if (l[lk].n) {
-            if (first < 0) first = lk;
-            last = lk;
-        }
-    for (int lk = 0; lk < 3; ++lk) {
+    const int first = l[0].n ? 0 : 1, last = l[1].n ? 1 : 0;
+    for (int lk = 0; lk < 2; ++lk) {
         if (!l[lk].n) continue;
-        const hipError_t e = launch_ns_phase(kind, lk == 1, lk == 2 ? 256 : 128, l[lk].d, l[lk].n, desc, pa, stream,
+        const hipError_t e = launch_ns_phase(kind, lk == 1, kTileBf16, l[lk].d, l[lk].n, desc, pa, stream,
                                              lk == first ? e0 : nullptr, lk == last ? e1 : nullptr);
         if (e != hipSuccess) return e;
     }
@@ -776,6 +776,20 @@ muon_status enqueue_step(muon_handle* h, const Plan& plan, const MatDesc* d_desc
     return MUON_OK;
 }
 
+// Debug handles: after the step, count the guard-band words that no longer
+// hold the pattern (the stream is waited for).
+muon_status check_guards(muon_handle* h, const Plan& plan, hipStream_t stream) {
+    uint32_t bad = 0;
+    hipError_t e = launch_fill_zero(plan.d_guard_bad, 16, stream);
+    if (e == hipSuccess) e = launch_guards(plan.ws, plan.d_guards, plan.n_guards, plan.d_guard_bad, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(&bad, plan.d_guard_bad, sizeof bad, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(h, e, "guard band check");
+    if (bad != 0)
+        return fail(h, MUON_ERR_HIP, "debug check: %u words of the workspace guard bands were overwritten", bad);
+    return MUON_OK;
+}
+
 muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hparams* hp, hipStream_t stream,
                  Plan** used) {
     const int n = int(mats.size());
@@ -802,7 +816,9 @@ muon_status run(muon_handle* h, const std::vector<MatIn>& mats, const muon_hpara
     st = select_table(h, plan.tabs, desc, capturing, stream, &d_desc);
     if (st != MUON_OK) return st;
     if (used) *used = pp;
-    return enqueue_step(h, plan, d_desc, n, hp, stream);
+    st = enqueue_step(h, plan, d_desc, n, hp, stream);
+    if (st == MUON_OK && plan.n_guards > 0 && !capturing) st = check_guards(h, plan, stream);
+    return st;
 }
 
 // ---- the no-allocation variant: everything in the device's static scratch ----
@@ -831,11 +847,11 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
     PlanLayout L;
     muon_status st = layout_plan(h, mats, f32c, L);
     if (st != MUON_OK) return st;
-    // scratch layout: workspace | 9 tile lists | units | partials | norms | descriptors
+    // scratch layout: workspace | 6 tile lists | units | partials | norms | descriptors
     size_t off = align256(L.ws_bytes);
-    size_t list_off[3][3];
+    size_t list_off[3][2];
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 3; ++lk) {
+        for (int lk = 0; lk < 2; ++lk) {
             list_off[l][lk] = off;
             off = align256(off + sizeof(Tile) * L.lists[l][lk].size());
         }
@@ -858,7 +874,7 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
     Plan plan;   // views into the scratch: owns no device memory
     TileList* tl[3] = {plan.gram, plan.poly, plan.axpy};
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 3; ++lk) {
+        for (int lk = 0; lk < 2; ++lk) {
             tl[l][lk].d = reinterpret_cast<Tile*>(base + list_off[l][lk]);
             tl[l][lk].n = int(L.lists[l][lk].size());
         }
@@ -884,7 +900,7 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
         sd.desc_valid = false;
         e = launch_fill_zero(base, L.ws_bytes, stream);
         for (int l = 0; e == hipSuccess && l < 3; ++l)
-            for (int lk = 0; e == hipSuccess && lk < 3; ++lk)
+            for (int lk = 0; e == hipSuccess && lk < 2; ++lk)
                 if (!L.lists[l][lk].empty())
                     e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
                                        hipMemcpyHostToDevice, stream);
@@ -921,7 +937,8 @@ int muon_abi_version(void) { return MUON_ABI_VERSION; }
 muon_status muon_init(muon_handle** out, int device, uint32_t flags) {
     if (!out) return MUON_ERR_INVALID_ARG;
     *out = nullptr;
-    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC | MUON_INIT_PROFILE_ROLES(kRoleBits))) return MUON_ERR_INVALID_ARG;
+    if (flags & ~(MUON_INIT_PROFILE | MUON_INIT_FAIL_ALLOC | MUON_INIT_DEBUG | MUON_INIT_PROFILE_ROLES(kRoleBits)))
+        return MUON_ERR_INVALID_ARG;
     int count = 0;
     if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
         (void)hipGetLastError();

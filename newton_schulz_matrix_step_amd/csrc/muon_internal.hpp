@@ -99,6 +99,12 @@ hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const double* p
 // workgroup per momentum-pass unit; the others return at once).
 hipError_t launch_rescale(const Unit* units, int n_units, const MatDesc* mats, const NormScale* norm, char* ws,
                           hipStream_t s, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+// Debug guard bands after every workspace buffer: kGuardBytes of a fixed
+// pattern.  bad == nullptr: write the pattern; otherwise add to *bad the
+// number of 4-byte words that differ from it.
+constexpr int kGuardBytes = 256;
+constexpr uint32_t kGuardPattern = 0xA5C3F00Du;
+hipError_t launch_guards(char* ws, const int64_t* offsets, int n_guards, uint32_t* bad, hipStream_t s);
 hipError_t launch_ns_phase(int kind, bool f32_compute, int tile, const Tile* tiles, int n_tiles,
                            const MatDesc* mats, PhaseArgs a, hipStream_t s,
                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);

@@ -130,18 +130,37 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(u32x4_t* p, size_t 
 }
 
 // ---------------------------------------------------------------------------
+// debug guard bands: write the pattern, or count the words that lost it
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void guard_kernel(char* ws, const int64_t* __restrict__ offsets, int n_guards,
+                                                         uint32_t* bad) {
+    constexpr int kWords = kGuardBytes / 4;
+    for (int g = blockIdx.x; g < n_guards; g += gridDim.x) {
+        GMEM uint32_t* p = gm(reinterpret_cast<uint32_t*>(ws + offsets[g]));
+        for (int i = threadIdx.x; i < kWords; i += kThreads) {
+            if (!bad) p[i] = kGuardPattern;
+            else if (p[i] != kGuardPattern) atomicAdd(bad, 1u);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // momentum + operand copy + partial sums of squares
 // ---------------------------------------------------------------------------
 // The sum of squares runs in double: u^2 of any finite float is finite there,
 // and the sum of 2^31 of them neither overflows nor loses the small terms, so
 // the norm is right at every gradient scale.  g and m are read once and m' is
-// written once (streaming accesses); the operand copy of u is read again by
-// the first iteration's products.
-#ifndef MUON_MOM_NT_U
-#define MUON_MOM_NT_U 0
-#endif
+// written once (streaming accesses, MUON_MOM_NT); the operand copy of u is
+// read again by the first iteration's products (plain stores: a streaming
+// store of it measured 7 % slower on the GPT-2 124M set).
 #ifndef MUON_MOM_NT
 #define MUON_MOM_NT 1
+#endif
+#ifndef MUON_MOM_FLAT
+#define MUON_MOM_FLAT 1
+#endif
+#ifndef MUON_MOM_UNROLL
+#define MUON_MOM_UNROLL 4
 #endif
 template <class T>
 __device__ __forceinline__ T mom_ld(const GMEM T* p) {
@@ -168,12 +187,98 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
     const int64_t ldu = md.Cp;
     double ss = 0.0;
 
-    if (md.vec_ok) {
+    // Contiguous rows (grad, momentum and the operand copy all with leading
+    // dimension C): the unit is one flat range of elements, taken in groups of
+    // 8 with no row arithmetic.
+    const bool flat = MUON_MOM_FLAT && md.vec_ok && md.ld_grad == C && (!has_mom || md.ld_mom == C) && ldu == C;
+    if (flat) {
+        constexpr int kU = MUON_MOM_UNROLL;
+        const int64_t e0 = int64_t(un.r0) * C;
+        const int n8 = (rows * C) >> 3;   // groups of 8 in the unit (C % 8 == 0)
+        const bool bf = md.io_dtype == 0;
+        const GMEM char* gbase = gm(static_cast<const char*>(md.grad));
+        GMEM float* mbase = gm(md.mom) + e0;
+        for (int base = threadIdx.x; base < n8; base += kThreads * kU) {
+            u32x4_t graw[kU][2];
+            f32x4_t mv[kU][2];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int q = base + u * kThreads;
+                if (q < n8) {
+                    const int64_t e = e0 + (int64_t(q) << 3);
+                    if (bf) {
+                        graw[u][0] = mom_ld(reinterpret_cast<const GMEM u32x4_t*>(gbase + e * 2));
+                    } else {
+                        const GMEM u32x4_t* gp = reinterpret_cast<const GMEM u32x4_t*>(gbase + e * 4);
+                        graw[u][0] = mom_ld(gp);
+                        graw[u][1] = mom_ld(gp + 1);
+                    }
+                    if (has_mom) {
+                        const GMEM f32x4_t* mp = reinterpret_cast<const GMEM f32x4_t*>(mbase + (int64_t(q) << 3));
+                        mv[u][0] = mom_ld(mp);
+                        mv[u][1] = mom_ld(mp + 1);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int q = base + u * kThreads;
+                if (q >= n8) continue;
+                float g[8];
+                if (bf) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        g[2 * k] = __uint_as_float(graw[u][0][k] << 16);
+                        g[2 * k + 1] = __uint_as_float(graw[u][0][k] & 0xFFFF0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        g[k] = __uint_as_float(graw[u][0][k]);
+                        g[4 + k] = __uint_as_float(graw[u][1][k]);
+                    }
+                }
+                float uu[8];
+                if (has_mom) {
+                    f32x4_t m0 = mv[u][0], m1 = mv[u][1];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        m0[k] = fmaf(beta, m0[k], g[k]);
+                        m1[k] = fmaf(beta, m1[k], g[4 + k]);
+                    }
+                    GMEM f32x4_t* mp = reinterpret_cast<GMEM f32x4_t*>(mbase + (int64_t(q) << 3));
+                    mom_st(mp, m0);
+                    mom_st(mp + 1, m1);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        uu[k] = nest ? fmaf(beta, m0[k], g[k]) : m0[k];
+                        uu[4 + k] = nest ? fmaf(beta, m1[k], g[4 + k]) : m1[k];
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) uu[k] = g[k];
+                }
+                // squares summed as a tree, one dependent add into ss per group
+                double sq[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) sq[k] = double(uu[k]) * double(uu[k]);
+                ss += ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+                const int64_t e = e0 + (int64_t(q) << 3);
+                if (F32C) {
+                    GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + e));
+                    up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
+                    up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
+                } else {
+                    u32x4_t w;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) w[k] = pack_bf16x2(uu[2 * k], uu[2 * k + 1]);
+                    *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + e)) = w;
+                }
+            }
+        }
+    } else if (md.vec_ok) {
         // kU groups of 8 columns per thread per pass: every load of the pass is
         // issued before the first use, so each thread keeps kU x 48 bytes in flight
-#ifndef MUON_MOM_UNROLL
-#define MUON_MOM_UNROLL 4
-#endif
         constexpr int kU = MUON_MOM_UNROLL;
         const int gpr = C >> 3;  // groups of 8 columns per row
         const int total = rows * gpr;
@@ -244,24 +349,19 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const Unit* __restri
 #pragma unroll
                     for (int q = 0; q < 8; ++q) uu[q] = g[q];
                 }
+                double sq[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) ss = fma(double(uu[q]), double(uu[q]), ss);
+                for (int q = 0; q < 8; ++q) sq[q] = double(uu[q]) * double(uu[q]);
+                ss += ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
                 if (F32C) {
                     GMEM f32x4_t* up = gm(reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(ub) + row[u] * ldu + col[u]));
-                    if (MUON_MOM_NT_U) {
-                        st_nt(up, f32x4_t{uu[0], uu[1], uu[2], uu[3]});
-                        st_nt(up + 1, f32x4_t{uu[4], uu[5], uu[6], uu[7]});
-                    } else {
-                        up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
-                        up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
-                    }
+                    up[0] = f32x4_t{uu[0], uu[1], uu[2], uu[3]};
+                    up[1] = f32x4_t{uu[4], uu[5], uu[6], uu[7]};
                 } else {
                     u32x4_t w;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(uu[2 * q], uu[2 * q + 1]);
-                    GMEM u32x4_t* up = gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + row[u] * ldu + col[u]));
-                    if (MUON_MOM_NT_U) st_nt(up, w);
-                    else *up = w;
+                    *gm(reinterpret_cast<u32x4_t*>(reinterpret_cast<uint16_t*>(ub) + row[u] * ldu + col[u])) = w;
                 }
             }
         }
@@ -312,7 +412,8 @@ __global__ __launch_bounds__(kThreads) void finalize_norm_kernel(const MatDesc* 
     if (threadIdx.x == 0) {
         const double nu = sqrt(red[0]);
         int k = 0;
-        if (nu > 0.0 && nu < __builtin_inf() && (nu < 0x1p-30 || nu > 0x1p+30)) k = ilogb(nu);
+        if (nu > 0.0 && nu < __builtin_inf() && (nu < ldexp(1.0, -kSafeExp) || nu > ldexp(1.0, kSafeExp)))
+            k = ilogb(nu);
         const double inv = 1.0 / (nu + double(eps));
         NormScale ns;
         ns.inv = float(inv);
@@ -325,26 +426,29 @@ __global__ __launch_bounds__(kThreads) void finalize_norm_kernel(const MatDesc* 
 
 // Operand copy of u -> u 2^-k for the entries whose norm lies outside the
 // safe range (exact: a power-of-two scaling of values far from the ends of
-// the exponent range).
-__global__ __launch_bounds__(kThreads) void rescale_kernel(const Unit* __restrict__ units,
+// the exponent range).  Workgroups stride over the momentum-pass units; in
+// the common case every unit's k is 0 and each workgroup only reads them.
+__global__ __launch_bounds__(kThreads) void rescale_kernel(const Unit* __restrict__ units, int n_units,
                                                            const MatDesc* __restrict__ mats,
                                                            const NormScale* __restrict__ norm, char* ws) {
-    const Unit un = units[blockIdx.x];
-    const int k = norm[un.mat].k;
-    if (k == 0) return;
-    const MatDesc& md = mats[un.mat];
-    const bool F32C = md.f32 != 0;
-    const int C = md.C;
-    const int total = (un.r1 - un.r0) * C;
-    for (int idx = threadIdx.x; idx < total; idx += kThreads) {
-        const int rr = idx / C;
-        const int64_t i = int64_t(un.r0 + rr) * md.Cp + (idx - rr * C);
-        if (F32C) {
-            GMEM float* p = gm(reinterpret_cast<float*>(ws + md.off_u)) + i;
-            *p = ldexpf(*p, -k);
-        } else {
-            GMEM uint16_t* p = gm(reinterpret_cast<uint16_t*>(ws + md.off_u)) + i;
-            *p = f32_to_bf16(ldexpf(bf16_to_f32(*p), -k));
+    for (int ui = blockIdx.x; ui < n_units; ui += gridDim.x) {
+        const Unit un = units[ui];
+        const int k = norm[un.mat].k;
+        if (k == 0) continue;
+        const MatDesc& md = mats[un.mat];
+        const bool F32C = md.f32 != 0;
+        const int C = md.C;
+        const int total = (un.r1 - un.r0) * C;
+        for (int idx = threadIdx.x; idx < total; idx += kThreads) {
+            const int rr = idx / C;
+            const int64_t i = int64_t(un.r0 + rr) * md.Cp + (idx - rr * C);
+            if (F32C) {
+                GMEM float* p = gm(reinterpret_cast<float*>(ws + md.off_u)) + i;
+                *p = ldexpf(*p, -k);
+            } else {
+                GMEM uint16_t* p = gm(reinterpret_cast<uint16_t*>(ws + md.off_u)) + i;
+                *p = f32_to_bf16(ldexpf(bf16_to_f32(*p), -k));
+            }
         }
     }
 }
@@ -684,10 +788,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 template <int BM, int BK_ = 64>
 struct BfCfg {
     static constexpr int BK = BK_;                // k per LDS stage (32 or 64)
-    // LDS stages (ring; the epilogue reuses them): 128-wide tiles within
-    // 64 KB so two workgroups share a CU; 256-wide tiles take the whole
-    // 160 KB of one CU
-    static constexpr int LDS_BUDGET = BM == 256 ? 160 * 1024 : 64 * 1024;
+    // LDS stages (ring; the epilogue reuses them), within 64 KB so two
+    // workgroups share a CU
+    static constexpr int LDS_BUDGET = 64 * 1024;
     static constexpr int NST = LDS_BUDGET / (2 * BM * BK * 2) > 8 ? 8 : LDS_BUDGET / (2 * BM * BK * 2);
     static constexpr int CPK = BK / 8;            // 16-byte chunks per [row][BK] row
     static constexpr int WT = BM / 2;             // wave tile edge
@@ -700,10 +803,6 @@ struct BfCfg {
     static constexpr int RPK = 64 / CPR;          // [k][BM] rows per 1 KB
 };
 constexpr int kBK = 64;
-// k per LDS stage: 64 on 128-wide tiles; 32 on 256-wide ones (five stages of
-// 32 KB keep four k blocks of loads in flight)
-template <int BM>
-constexpr int bk_of() { return BM == 256 ? 32 : kBK; }
 
 // Swizzle of the 16-byte chunks of a [k][BM] LDS row.  A ds_read_b64_tr_b16
 // group of 16 lanes reads rows k0..k0+3 (4 rows x 32 bytes): bits 1-2 spread
@@ -1380,13 +1479,14 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
             }
     }
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i) {
 #pragma unroll
         for (int j = 0; j < TI; ++j) {
             const int rl = 16 * i + l16, cl = 16 * j + g4;
+            const u32x2_t& ava = av[i][j];
             f32x4_t w;
             if constexpr (POLY) {
-                const f32x4_t a = dec4(u32x4_t{av[i][j][0], av[i][j][1], 0u, 0u}, 0);
+                const f32x4_t a = dec4(u32x4_t{ava[0], ava[1], 0u, 0u}, 0);
                 w = x.b * a + x.c * acc[i][j];
             } else {
                 w = acc[i][j] * x.scl;
@@ -1408,16 +1508,17 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
                     if (r <= c + k) o[k] = h[k];
             }
         }
+    }
     sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
-__global__ __launch_bounds__(kThreads, BM == 128 ? 2 : 1) void ns_gemm_bf16(const Tile* __restrict__ tiles,
+__global__ __launch_bounds__(kThreads, 2) void ns_gemm_bf16(const Tile* __restrict__ tiles,
                                                             const MatDesc* __restrict__ mats, PhaseArgs pa,
                                                             int n_tiles) {
-    constexpr int BK = bk_of<BM>();
+    constexpr int BK = kBK;
     using C = BfCfg<BM, BK>;
     constexpr int TI = C::TI, WT = C::WT;
     // operand stages; afterwards the epilogue's per-wave regions
@@ -1539,6 +1640,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_guards(char* ws, const int64_t* offsets, int n_guards, uint32_t* bad, hipStream_t s) {
+    if (n_guards <= 0) return hipSuccess;
+    const int grid = n_guards < 1024 ? n_guards : 1024;
+    hipLaunchKernelGGL(guard_kernel, dim3(grid), dim3(kThreads), 0, s, ws, offsets, n_guards, bad);
+    return hipGetLastError();
+}
+
 hipError_t launch_momentum(const Unit* units, int n_units, const MatDesc* mats, MomentumArgs a, hipStream_t s,
                            hipEvent_t ev0, hipEvent_t ev1) {
     if (n_units <= 0) return hipSuccess;
@@ -1557,7 +1665,9 @@ hipError_t launch_finalize_norm(const MatDesc* mats, int n_mats, const double* p
 hipError_t launch_rescale(const Unit* units, int n_units, const MatDesc* mats, const NormScale* norm, char* ws,
                           hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_units <= 0) return hipSuccess;
-    hipExtLaunchKernelGGL(rescale_kernel, dim3(n_units), dim3(kThreads), 0, s, ev0, ev1, 0, units, mats, norm, ws);
+    const int grid = n_units < 1024 ? n_units : 1024;
+    hipExtLaunchKernelGGL(rescale_kernel, dim3(grid), dim3(kThreads), 0, s, ev0, ev1, 0, units, n_units, mats, norm,
+                          ws);
     return hipGetLastError();
 }
 
@@ -1584,16 +1694,14 @@ static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, con
                               mats, a);
         return;
     }
-    if (tile == 256)
-        launch_bf16<KIND, 256>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
-    else
-        launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
+    (void)tile;
+    launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    if (tile != 128 && !(tile == 256 && !f32c)) return hipErrorInvalidValue;
+    if (tile != 128) return hipErrorInvalidValue;
     switch (kind) {
         case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;

@@ -1,7 +1,7 @@
 // Test infrastructure: runs muon_step and muon_adamw_step of the library, built
 // against the CPU stand-in of HIP (tests/emu/hip), on exactly sized host
 // buffers, so AddressSanitizer reports any access outside a caller buffer or
-// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT [GRAD [NOALLOC]]]]]
+// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT [GRAD [NOALLOC [DEBUG]]]]]]
 //   SHAPES "RxC,RxC,...", DTYPE 0 = bf16, 1 = f32 (also selects fp32 compute),
 //   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks,
 //   LD_PAD extra elements per row (views into wider buffers), SHIFT elements
@@ -31,6 +31,7 @@ int main(int argc, char** argv) {
     const long shift = argc > 6 ? std::atol(argv[6]) : 0;
     const double gval = argc > 7 ? std::atof(argv[7]) : 0.0;
     const bool noalloc = argc > 8 && std::atoi(argv[8]) != 0;
+    const bool debug = argc > 9 && std::atoi(argv[9]) != 0;
     std::vector<std::pair<long, long>> shapes;
     for (size_t p = 0; p < spec.size();) {
         size_t q = spec.find(',', p);
@@ -75,7 +76,7 @@ int main(int argc, char** argv) {
         mats.push_back(m);
     }
     muon_handle* h = nullptr;
-    if (muon_init(&h, 0, 0) != MUON_OK) return 3;
+    if (muon_init(&h, 0, debug ? MUON_INIT_DEBUG : 0u) != MUON_OK) return 3;
     const float sched[6] = {3.4445f, -4.7750f, 2.0315f, 1.5f, -0.5f, 0.0f};
     muon_hparams hp{0.02f, 0.95f, 0.01f, 1e-7f, 3.4445f, -4.775f, 2.0315f, 1, ns,
                     dtype == 0 ? MUON_COMPUTE_BF16 : MUON_COMPUTE_FP32, ns == 2 ? sched : nullptr};

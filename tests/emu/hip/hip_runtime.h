@@ -75,6 +75,7 @@ inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
 inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 template <class T> inline T __shfl_xor(T v, int, int) { return v; }
 inline void __syncthreads() {}
+inline unsigned atomicAdd(unsigned* p, unsigned v) { const unsigned o = *p; *p = o + v; return o; }
 
 #define __builtin_amdgcn_readfirstlane(x) (x)
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)

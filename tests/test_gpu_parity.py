@@ -422,6 +422,26 @@ def test_save_reload_continue_is_bitwise_unbroken():
         assert np.array_equal(m_a[i].cpu().numpy(), m_c[i].cpu().numpy())
 
 
+def test_debug_guard_bands():
+    """A handle created with MUON_INIT_DEBUG puts a guard band after every
+    workspace buffer and checks all of them after each step: over mixed
+    shapes (float32 small entries, bf16 ones, transposed, blocked) and three
+    steps no band is touched, and the results equal a plain handle's bit for
+    bit (the bands only move buffers apart)."""
+    wl = _wl("guards", [(300, 100), (128, 384), (96, 96), (48, 40), (17, 1), (256, 256)], steps=3, nesterov=True,
+             weight_decay=0.01, blocks=((0, 0), (64, 0), (0, 0), (0, 0), (0, 0), (128, 128)))
+    import newton_schulz_matrix_step_amd as nsm
+    h = nsm.muon_init(0, nsm.MUON_INIT_DEBUG)
+    try:
+        a = run_gpu(wl, 3, list(range(6)), handle=h)
+    finally:
+        nsm.muon_destroy(h)
+    b = run_gpu(wl, 3, list(range(6)))
+    for i in range(6):
+        for ra, rb in zip(a[i], b[i]):
+            assert np.array_equal(ra.o, rb.o) and np.array_equal(ra.w_new, rb.w_new) and np.array_equal(ra.m_new, rb.m_new)
+
+
 def test_forced_allocation_failure():
     """A handle created with MUON_INIT_FAIL_ALLOC fails every workspace or plan
     allocation: both entry points report MUON_ERR_OOM and change nothing."""
