@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_CLOCK_GHZ = 2.4           # MI355X peak engine clock, which the MFMA peaks assume
 
 METRIC = "Muon steps/sec + NS TFLOP/s (% bf16 MFMA peak), GPT-2-124M matrix set, 1 GPU"
 DEFAULT_WORKLOAD = "gpt2-124m-hidden"
@@ -122,12 +123,10 @@ def kernel_source_hash() -> str:
     return hsh.hexdigest()
 
 
-def recorded_traffic(role: str, workload_name: str):
-    """HBM bytes per launch of ``role`` on ``workload_name`` from the counter
-    summary under profiles/ (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled
-    by the same counters' reading for a plain copy of known size), or None when
-    there is no summary or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{role}_{workload_name}.md")
+def _recorded_values(name: str):
+    """The "- `key`: `value`" lines of profiles/<name>.md, or None when the file
+    is missing or the kernel sources changed since its counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -138,29 +137,52 @@ def recorded_traffic(role: str, workload_name: str):
                 rec[k.strip("`")] = v.strip().strip("`")
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
+    return rec
+
+
+def recorded_traffic(role: str, workload_name: str):
+    """HBM bytes per launch of ``role`` on ``workload_name`` from the counter
+    summary under profiles/ (rocprofv3 FETCH_SIZE and WRITE_SIZE passes, scaled
+    by the same counters' reading for a plain copy of known size), or None when
+    there is no summary or the kernel sources changed since it was taken."""
+    rec = _recorded_values(f"traffic_{role}_{workload_name}")
     try:
         return {"fetch": float(rec["fetch_bytes_per_launch"]), "write": float(rec["write_bytes_per_launch"])}
-    except (KeyError, ValueError):
+    except (TypeError, KeyError, ValueError):
+        return None
+
+
+def recorded_clock(role: str, workload_name: str):
+    """Mean shader clock (GHz) during launches of ``role`` on ``workload_name``:
+    rocprofv3's GRBM_COUNT (cycles, summed over the XCDs) over the dispatch's
+    duration, from profiles/clock_<workload>.md; None as for recorded_traffic."""
+    rec = _recorded_values(f"clock_{workload_name}")
+    try:
+        return float(rec[f"clock_ghz_{role}"])
+    except (TypeError, KeyError, ValueError):
         return None
 
 
 def summarize_counters(paths):
     """Mean per dispatch of every counter, per kernel, from rocprofv3
-    ``*_counter_collection.csv`` files (rows of one dispatch are summed)."""
+    ``*_counter_collection.csv`` files (rows of one dispatch are summed), with
+    the mean duration of those dispatches (their start and end timestamps)."""
     import csv
     from collections import defaultdict
     tot = defaultdict(float)
-    disp = defaultdict(set)
+    disp = defaultdict(dict)
     for p in paths:
         with open(p) as f:
             for r in csv.DictReader(f):
                 key = (r["Kernel_Name"], r["Counter_Name"])
                 tot[key] += float(r["Counter_Value"])
-                disp[key].add(r["Dispatch_Id"])
+                disp[key][(p, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     rows = []
     for (kname, cname), v in sorted(tot.items()):
-        nd = len(disp[(kname, cname)])
-        rows.append({"kernel": kname, "counter": cname, "dispatches": nd, "mean_per_dispatch": v / nd})
+        d = disp[(kname, cname)]
+        nd = len(d)
+        rows.append({"kernel": kname, "counter": cname, "dispatches": nd, "mean_per_dispatch": v / nd,
+                     "mean_dispatch_ns": sum(d.values()) / nd})
     return rows
 
 
@@ -618,6 +640,14 @@ def main():
         roofline["traffic"] = round(tr["fetch"] + tr["write"])
         roofline["traffic_fetch"] = round(tr["fetch"])
         roofline["traffic_write"] = round(tr["write"])
+    # the published MFMA peak assumes the 2.4 GHz peak engine clock; under a
+    # sustained matrix load the chip runs slower, so the fraction of the peak
+    # at the clock the kernel actually ran at is reported beside it
+    clk = recorded_clock(dom, wl.name)
+    roofline["clock_ghz"] = clk
+    if clk is not None:
+        roofline["mfma_peak_at_clock"] = round(peak * clk / PEAK_CLOCK_GHZ, 1)
+        roofline["mfma_frac_at_clock"] = round(mfma_frac * PEAK_CLOCK_GHZ / clk, 4)
     mom = kernels.get("momentum_norm", {})
 
     out = {
