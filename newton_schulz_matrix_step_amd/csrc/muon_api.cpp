@@ -70,6 +70,22 @@ constexpr int kItemRowsSym = 8;
 constexpr int kItemRowsAxpyWhole = 8;
 constexpr int kItemRowsAxpy = 4;
 
+// Tile lists per phase, one per kernel: [0] bf16 iterations on 128-wide
+// tiles, [1] float32 iterations, [2] the bf16 AXPY of large matrices on
+// 256-wide tiles (GRAM and POLY lists [2] stay empty).  A matrix may take the
+// wide AXPY when its padded shape is a multiple of 256 and both sides are at
+// least kWideMinDim (smaller ones have too few wide tiles to fill the CUs:
+// 768-wide matrices measured 3 % slower on them, 1024 x 4096 ones 7 % faster).
+// The wide list is used only when such matrices hold at least half of the
+// AXPY's flops: a phase split over two launches waits for the first one's
+// tail (the MoE stack's four 2048 x 2048 matrices beside 128 experts of
+// 2048 x 1408 measured 4 % slower split).
+constexpr int kListKinds = 3;
+#ifndef MUON_WIDE_MIN
+#define MUON_WIDE_MIN 1024
+#endif
+constexpr int kWideMinDim = MUON_WIDE_MIN;
+
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Pinned host slots for descriptor uploads: a slot is reused once the copy out
@@ -112,7 +128,7 @@ struct Plan {
     int n = 0;
     std::vector<MatDesc> geom;     // static part of every descriptor
     // per phase, one list per kernel: [0] bf16-iteration entries, [1] float32 entries
-    TileList gram[2], poly[2], axpy[2];
+    TileList gram[kListKinds], poly[kListKinds], axpy[kListKinds];
     Unit* d_units = nullptr;
     int n_units = 0;
     double* d_partials = nullptr;
@@ -204,7 +220,7 @@ void free_tables(TableSet<D>& ts) {
 }
 
 void free_plan(Plan& p) {
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kListKinds; ++m) {
         (void)hipFree(p.gram[m].d);
         (void)hipFree(p.poly[m].d);
         (void)hipFree(p.axpy[m].d);
@@ -397,7 +413,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct PlanLayout {
     std::vector<MatDesc> geom;
     std::vector<Unit> units;
-    std::vector<Tile> lists[3][2];   // [phase: GRAM, POLY, AXPY][0 bf16 entries, 1 float32 entries]
+    std::vector<Tile> lists[3][kListKinds];   // [phase: GRAM, POLY, AXPY][list kind]
     std::vector<int64_t> guards;     // debug handles: workspace offsets of the guard bands
     size_t ws_bytes = 0;
 };
@@ -453,16 +469,32 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         d.nunits = int32_t(units.size()) - d.unit0;
         geom[i] = d;
     }
-    // Newton-Schulz tile edge: 128 x 128 for every phase and both modes.  Two
+    // Newton-Schulz tile edge: 128 x 128 for every phase and both modes, and
+    // 256 x 256 for the bf16 AXPY of large matrices (kListKinds).  Two 128-wide
     // workgroups share a CU, so one tile's epilogue overlaps another's main
     // loop; AXPY tiles of this size also keep their quadrant of X from the
-    // operand stream.  256-wide tiles (one workgroup of four 128 x 128 waves
-    // per CU, half the operand traffic and LDS reads per flop, software
-    // pipelined) measured no faster on any workload and slower on most.
-    constexpr int T = kTileBf16;
+    // operand stream.  256-wide tiles of four 128 x 128 waves (one per SIMD)
+    // measured no faster on any workload; the wide AXPY's eight 128 x 64 waves
+    // (two per SIMD) are 7-10 % faster on large matrices.
     static_assert(kTileBf16 == kTileF32, "one tile edge for both modes");
-    // list of entry i: 0 bf16 iteration, 1 float32 iteration
-    auto list_kind = [&](int i) { return geom[i].f32 ? 1 : 0; };
+    auto tile_of = [](int lk) { return lk == 2 ? kTileWide : kTileBf16; };
+    auto wide_ok = [&](const MatDesc& d) {
+        return !d.f32 && d.Rp % kTileWide == 0 && d.Cp % kTileWide == 0 && std::min(d.R, d.C) >= kWideMinDim;
+    };
+    double axpy_flops = 0.0, wide_flops = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (geom[i].f32) continue;
+        const double f = double(geom[i].R) * geom[i].C * geom[i].m;
+        axpy_flops += f;
+        if (wide_ok(geom[i])) wide_flops += f;
+    }
+    const bool use_wide = wide_flops >= 0.5 * axpy_flops && wide_flops > 0.0;
+    // list of entry i in a phase (see kListKinds)
+    auto list_kind = [&](int kind, int i) {
+        const MatDesc& d = geom[i];
+        if (d.f32) return 1;
+        return kind == PH_AXPY && use_wide && wide_ok(d) ? 2 : 0;
+    };
     // Tile lists, one per phase and per iteration precision (bf16 and float32
     // entries run different kernels).  Workgroup b runs on XCD b % 8, and each
     // XCD has its own L2, so every list is 8 chunks, one per XCD: chunk x
@@ -477,6 +509,7 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
     // tiles differently, so each gets its own list.
     auto build_list = [&](int kind, int lk, std::vector<Tile>& out) {
         const bool sym = kind != PH_AXPY;
+        const int T = tile_of(lk);
         struct Item {
             int mat, a0;
             int64_t w;
@@ -493,7 +526,7 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         };
         auto item_rows = [&](int tm) { return sym ? kItemRowsSym : (tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy); };
         for (int i = 0; i < n; ++i) {
-            if (list_kind(i) != lk) continue;
+            if (list_kind(kind, i) != lk) continue;
             int tm, tn;
             dims(geom[i], tm, tn);
             const int IR = item_rows(tm);
@@ -530,14 +563,15 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         out.assign(8 * chunk, Tile{-1, 0, 0, 0});
         for (int x = 0; x < 8; ++x) std::copy(bins[x].begin(), bins[x].end(), out.begin() + x * chunk);
     };
-    std::vector<Tile> lists[3][2];
-    for (int lk = 0; lk < 2; ++lk) {
+    std::vector<Tile> lists[3][kListKinds];
+    for (int lk = 0; lk < kListKinds; ++lk) {
         build_list(PH_GRAM, lk, lists[0][lk]);
         build_list(PH_POLY, lk, lists[1][lk]);
         build_list(PH_AXPY, lk, lists[2][lk]);
     }
     // every tile's operand panels must lie inside the padded workspace buffers
-    for (int lk = 0; lk < 2; ++lk) {
+    for (int lk = 0; lk < kListKinds; ++lk) {
+        const int T = tile_of(lk);
         for (int l = 0; l < 2; ++l)
             for (const Tile& t : lists[l][lk]) {
                 if (t.mat < 0) continue;
@@ -556,7 +590,7 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
     L.geom = std::move(geom);
     L.units = std::move(units);
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 2; ++lk) L.lists[l][lk] = std::move(lists[l][lk]);
+        for (int lk = 0; lk < kListKinds; ++lk) L.lists[l][lk] = std::move(lists[l][lk]);
     L.ws_bytes = off;
     return MUON_OK;
 }
@@ -581,7 +615,7 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     TileList* tl[3] = {q->gram, q->poly, q->axpy};
     bool ok = true;
     for (int l = 0; ok && l < 3; ++l)
-        for (int lk = 0; ok && lk < 2; ++lk)
+        for (int lk = 0; ok && lk < kListKinds; ++lk)
             if (!L.lists[l][lk].empty())
                 ok = dmalloc(reinterpret_cast<void**>(&tl[l][lk].d), sizeof(Tile) * L.lists[l][lk].size());
     ok = ok && dmalloc(reinterpret_cast<void**>(&q->d_units), sizeof(Unit) * L.units.size()) &&
@@ -603,7 +637,7 @@ muon_status build_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32c
     q->ws_bytes = off;
     hipError_t e = launch_fill_zero(q->ws, off, stream);
     for (int l = 0; e == hipSuccess && l < 3; ++l)
-        for (int lk = 0; e == hipSuccess && lk < 2; ++lk)
+        for (int lk = 0; e == hipSuccess && lk < kListKinds; ++lk)
             if (!L.lists[l][lk].empty()) {
                 e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
                                    hipMemcpyHostToDevice, stream);
@@ -657,16 +691,22 @@ hipError_t timed(muon_handle* h, int role, F&& launch, bool events = true) {
     return e;
 }
 
-// One phase over its tile lists (bf16 entries, then float32 entries); on a
-// profiling handle the phase is timed as one, from the first launch's start
-// to the last one's end.
-hipError_t launch_phase_lists(int kind, const TileList (&l)[2], const MatDesc* desc, const PhaseArgs& pa,
+// One phase over its tile lists (wide bf16 tiles first, then 128-wide bf16,
+// then float32); on a profiling handle the phase is timed as one, from the
+// first launch's start to the last one's end.
+hipError_t launch_phase_lists(int kind, const TileList (&l)[kListKinds], const MatDesc* desc, const PhaseArgs& pa,
                               hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-    const int first = l[0].n ? 0 : 1, last = l[1].n ? 1 : 0;
-    for (int lk = 0; lk < 2; ++lk) {
+    static constexpr int kOrder[kListKinds] = {2, 0, 1};
+    int first = -1, last = -1;
+    for (int lk : kOrder)
+        if (l[lk].n) {
+            if (first < 0) first = lk;
+            last = lk;
+        }
+    for (int lk : kOrder) {
         if (!l[lk].n) continue;
-        const hipError_t e = launch_ns_phase(kind, lk == 1, kTileBf16, l[lk].d, l[lk].n, desc, pa, stream,
-                                             lk == first ? e0 : nullptr, lk == last ? e1 : nullptr);
+        const hipError_t e = launch_ns_phase(kind, lk == 1, lk == 2 ? kTileWide : kTileBf16, l[lk].d, l[lk].n, desc,
+                                             pa, stream, lk == first ? e0 : nullptr, lk == last ? e1 : nullptr);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -849,9 +889,9 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
     if (st != MUON_OK) return st;
     // scratch layout: workspace | 6 tile lists | units | partials | norms | descriptors
     size_t off = align256(L.ws_bytes);
-    size_t list_off[3][2];
+    size_t list_off[3][kListKinds];
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 2; ++lk) {
+        for (int lk = 0; lk < kListKinds; ++lk) {
             list_off[l][lk] = off;
             off = align256(off + sizeof(Tile) * L.lists[l][lk].size());
         }
@@ -874,7 +914,7 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
     Plan plan;   // views into the scratch: owns no device memory
     TileList* tl[3] = {plan.gram, plan.poly, plan.axpy};
     for (int l = 0; l < 3; ++l)
-        for (int lk = 0; lk < 2; ++lk) {
+        for (int lk = 0; lk < kListKinds; ++lk) {
             tl[l][lk].d = reinterpret_cast<Tile*>(base + list_off[l][lk]);
             tl[l][lk].n = int(L.lists[l][lk].size());
         }
@@ -900,7 +940,7 @@ muon_status run_static(muon_handle* h, const std::vector<MatIn>& mats, const muo
         sd.desc_valid = false;
         e = launch_fill_zero(base, L.ws_bytes, stream);
         for (int l = 0; e == hipSuccess && l < 3; ++l)
-            for (int lk = 0; e == hipSuccess && lk < 2; ++lk)
+            for (int lk = 0; e == hipSuccess && lk < kListKinds; ++lk)
                 if (!L.lists[l][lk].empty())
                     e = hipMemcpyAsync(tl[l][lk].d, L.lists[l][lk].data(), sizeof(Tile) * L.lists[l][lk].size(),
                                        hipMemcpyHostToDevice, stream);

@@ -151,8 +151,10 @@ constexpr int kMaxStaticDevices = 64;
 // Device address of the scratch on `device` (which must be current).
 hipError_t static_scratch_base(int device, char** base);
 
-// Tile edge of the Newton-Schulz GEMMs (both modes use 128 x 128 tiles).
+// Tile edge of the Newton-Schulz GEMMs (both modes use 128 x 128 tiles; the
+// bf16 AXPY of large matrices may use 256 x 256 tiles).
 constexpr int kTileF32 = 128;
 constexpr int kTileBf16 = 128;
+constexpr int kTileWide = 256;
 
 }  // namespace muon

@@ -1525,6 +1525,164 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
     sym_mirror<TI>(x, tt, row0, col0, lane);   // same wave wrote tt: program order suffices
 }
 
+// ---------------------------------------------------------------------------
+// Wide AXPY for large matrices: 256 x 256 output tiles, one workgroup of 8
+// waves per CU (two per SIMD), each wave a 128 x 64 block (8 x 4 MFMA tiles)
+// instead of 64 x 64.  Per flop it reads a quarter fewer fragment bytes from
+// LDS and streams half the operand bytes from L2 into LDS (the 128-wide
+// kernel's two workgroups of four 64 x 64 waves need about 190 B/clk of LDS
+// traffic per CU at the MFMA rate, more than the LDS delivers).  k blocks of
+// 64 through two 64 KB LDS stages.  Every output element sums k in the same
+// order as in the 128-wide kernel, so the two give bitwise equal results.
+// The epilogue runs the 128-wide kernel's per-quadrant epilogue on the wave's
+// two 64 x 64 halves, reading the bf16 X from memory (no operand-stream
+// capture: its registers do not fit beside the 128 accumulators).
+//
+// WideCfg<TM, TN, BK, NST>: TM x TN tile, (TM / 128) x (TN / 64) waves, LDS
+// stages of BK k (a ring of NST).  Measured alternative: 256 x 128 tiles of
+// four waves, two workgroups per CU, three 32-deep stages each: slower than
+// the 128-wide kernel.
+// ---------------------------------------------------------------------------
+template <int TM_, int TN_, int BK_, int NST_>
+struct WideCfg {
+    static constexpr int TM = TM_, TN = TN_, BK = BK_, NST = NST_;
+    static constexpr int WR = TM / 128, WC = TN / 64;   // waves along rows and columns
+    static constexpr int NW = WR * WC;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int OPA = TM * BK * 2, OPB = TN * BK * 2;   // LDS bytes of each operand stage
+    static constexpr int STB = OPA + OPB;
+    static constexpr int LPA = OPA / 1024 / NW, LPB = OPB / 1024 / NW;   // 1 KB loads per wave
+    static constexpr int LPS = LPA + LPB;
+    static_assert(LPA * 1024 * NW == OPA && LPB * 1024 * NW == OPB, "whole 1 KB loads per wave");
+    static_assert(LPS <= 8, "the next stage's loads go out between the 8 MFMA rows of a step");
+};
+using WCfg = WideCfg<kTileWide, kTileWide, 64, 2>;
+
+// One 1 KB load (block q of this wave's share) of a ROWS x BK operand stage,
+// with the layouts and swizzles of issue_operand (a [k][ROWS] row of 512
+// bytes maps to the banks exactly as a 256-byte one).
+template <int ROWS, int BK, int NW, bool KC>
+__device__ __forceinline__ void issue_operand_wide(char* __restrict__ lds, const char* __restrict__ g, int64_t ld,
+                                                   int row0, int k0, int wave, int lane, int q) {
+    constexpr int LPW = ROWS * BK * 2 / 1024 / NW;
+    const int blk = wave * LPW + q;
+    if (KC) {
+        constexpr int CPK = BK / 8;
+        constexpr int RB = 64 / CPK;
+        const int rl = lane / CPK;
+        const int c = (lane % CPK) ^ kcswz<CPK>(rl);
+        const uint32_t voff = uint32_t(rl * ld * 2 + c * 16);
+        lds_dma16s(g + (int64_t(row0 + blk * RB) * ld + k0) * 2, voff, lds + blk * 1024);
+    } else {
+        constexpr int CPR = ROWS / 8;
+        constexpr int RPK = 64 / CPR;
+        const int kl = lane / CPR;
+        const int c = (lane % CPR) ^ kswz(blk * RPK + kl);
+        const uint32_t voff = uint32_t(kl * ld * 2 + c * 16);
+        lds_dma16s(g + (int64_t(k0 + blk * RPK) * ld + row0) * 2, voff, lds + blk * 1024);
+    }
+}
+
+// Load q (operand A first, then operand B) of this wave's share of one stage.
+template <class C, bool AKC, bool BKC>
+__device__ __forceinline__ void issue_wide_load(char* __restrict__ st, const Operands& op, int row_a0, int row_b0,
+                                                int k0, int wave, int lane, int q) {
+    if (q < C::LPA) issue_operand_wide<C::TM, C::BK, C::NW, AKC>(st, op.a, op.lda, row_a0, k0, wave, lane, q);
+    else issue_operand_wide<C::TN, C::BK, C::NW, BKC>(st + C::OPA, op.b, op.ldb, row_b0, k0, wave, lane, q - C::LPA);
+}
+
+template <class C, bool AKC, bool BKC>
+__device__ __forceinline__ void mainloop_wide(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0,
+                                              int wave, int lane, f32x4_t (&acc)[8][4]) {
+    const int wr = (wave / C::WC) * 128, wc = (wave % C::WC) * 64;
+    const int nk = (op.K + C::BK - 1) / C::BK;
+    // prologue: stages 0 .. NST-2
+#pragma unroll
+    for (int s = 0; s < C::NST - 1; ++s)
+        if (s < nk) {
+#pragma unroll
+            for (int q = 0; q < C::LPS; ++q)
+                issue_wide_load<C, AKC, BKC>(smem + s * C::STB, op, row_a0, row_b0, s * C::BK, wave, lane, q);
+        }
+    for (int kb = 0; kb < nk; ++kb) {
+        // stage kb has landed once at most (stages issued after it) x LPS loads are pending
+        const int ahead = nk - 1 - kb;
+        const int pend = ahead < C::NST - 2 ? ahead : C::NST - 2;
+        static_for<0, C::NST - 1>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            if (pend == p) vm_wait<p * C::LPS>();
+        });
+        __syncthreads();   // every wave's share of stage kb is in LDS; stage kb-1 is free
+        const bool more = kb + C::NST - 1 < nk;
+        char* nxt = smem + ((kb + C::NST - 1) % C::NST) * C::STB;
+        const int k_nxt = (kb + C::NST - 1) * C::BK;
+        const char* sa = smem + (kb % C::NST) * C::STB;
+        const char* sb = sa + C::OPA;
+#pragma unroll
+        for (int s = 0; s < C::BK / 32; ++s) {
+            bf16x8_t fa[8], fb[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fa[i] = frag<C::TM, C::BK, AKC>(sa, wr + 16 * i, s, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[j] = frag<C::TN, C::BK, BKC>(sb, wc + 16 * j, s, lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // the next stage's loads go out one between each row of the
+                // first step's MFMAs, not all at once after the barrier (about
+                // 1 % faster)
+                if (s == 0 && i < C::LPS && more)
+                    issue_wide_load<C, AKC, BKC>(nxt, op, row_a0, row_b0, k_nxt, wave, lane, i);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int KIND, bool FIRST>
+__global__ __launch_bounds__(WCfg::THREADS, 8 / WCfg::NW) void ns_axpy_wide(const Tile* __restrict__ tiles,
+                                                                            const MatDesc* __restrict__ mats,
+                                                                            PhaseArgs pa, int n_tiles) {
+    static_assert(KIND == PH_AXPY || KIND == PH_AXPY_LAST, "AXPY phases only");
+    using C = WCfg;
+    constexpr int TI = 4;   // epilogue quadrant of 4 x 4 MFMA tiles
+    constexpr int EPI_AXPY_BYTES = 16 * (16 * TI + 4) * 4;
+    constexpr int LDS_BYTES = C::NST * C::STB;
+    static_assert(C::NW * EPI_AXPY_BYTES <= LDS_BYTES, "epilogue staging fits the operand stages");
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
+    if (t.mat < 0) return;
+    const MatDesc& md = mats[t.mat];
+    const Operands op = resolve_operands<KIND>(md, pa);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row_a0 = t.ti * C::TM, row_b0 = t.tj * C::TN;
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (op.a_kc && op.b_kc)   // transposed matrix: X^T B
+        mainloop_wide<C, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
+    else                      // B X
+        mainloop_wide<C, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+    __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+
+    constexpr bool LAST = KIND == PH_AXPY_LAST;
+    const AxpyCtx x = axpy_ctx<FIRST>(md, t, pa);
+    const HiCap<TI> cap{};   // not used: the epilogue reads the bf16 X from memory
+    const AxpyRaw<TI> w0[1]{};
+    float* stg = reinterpret_cast<float*>(smem + wave * EPI_AXPY_BYTES);
+    const int er0 = row_a0 + (wave / C::WC) * 128, ec0 = row_b0 + (wave % C::WC) * 64;
+    epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[0]), cap, w0, er0, ec0, lane,
+                                        stg);
+    epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[4]), cap, w0, er0 + 64, ec0,
+                                        lane, stg);
+}
+
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
 // term recomputed from the caller's momentum and gradient).
 template <int KIND, int BM, bool FIRST>
@@ -1707,14 +1865,26 @@ static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, con
                               mats, a);
         return;
     }
-    (void)tile;
+    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+        if (tile == kTileWide) {
+            if (a.iter == 1)
+                hipExtLaunchKernelGGL((ns_axpy_wide<KIND, true>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0, ev1,
+                                      0, tiles, mats, a, n_tiles);
+            else
+                hipExtLaunchKernelGGL((ns_axpy_wide<KIND, false>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0,
+                                      ev1, 0, tiles, mats, a, n_tiles);
+            return;
+        }
+    }
     launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
 
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    if (tile != 128) return hipErrorInvalidValue;
+    // 256-wide tiles: bf16 AXPY phases only
+    const bool wide_ok = tile == kTileWide && !f32c && (kind == PH_AXPY || kind == PH_AXPY_LAST);
+    if (tile != kTileBf16 && !wide_ok) return hipErrorInvalidValue;
     switch (kind) {
         case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
         case PH_POLY: launch_kind<PH_POLY>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;
@@ -1733,3 +1903,4 @@ hipError_t launch_direct_update(const Unit* units, int n_units, const MatDesc* m
 }
 
 }  // namespace muon
+

@@ -23,6 +23,7 @@ int emu_verbose = 0;
 
 int main(int argc, char** argv) {
     if (argc < 4) return 2;
+    emu_verbose = std::getenv("EMU_VERBOSE") != nullptr;   // list every launch on stderr
     const std::string spec = argv[1];
     const int ns = std::atoi(argv[2]);
     const int dtype = std::atoi(argv[3]);

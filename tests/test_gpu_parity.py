@@ -739,3 +739,31 @@ def test_small_matrices_run_in_float32():
     check_against_oracle(wl, {i: rec[i] for i in small}, 1e-4, report=rep)
     check_against_oracle(wl, {i: rec[i] for i in range(len(shapes)) if i not in small}, TOL_O_BF16)
     print("small matrices worst O rel err", max(e for (_, _, _, e) in rep))
+
+
+def test_wide_axpy_tiles():
+    """Large matrices (both sides at least 1024, padded shape a multiple of
+    256) run the AXPY on 256-wide tiles when they hold most of the phase's
+    flops.  Their results meet the oracle bars (a ragged 1000 x 2000 matrix
+    among them, every iteration kind over three steps) and equal bitwise those
+    of the 128-wide kernel, which the same matrices take when a larger
+    matrix that cannot use wide tiles (1152 padded rows) dominates the call:
+    both kernels sum every output element's k in the same order."""
+    base = workload("gpt2-124m-hidden")
+    shapes = [(1024, 2048), (2048, 1024), (1000, 2000), (1024, 1024), (300, 100)]
+
+    def mk(shp):
+        mats = tuple(MatSpec(r, c, f"m{i}") for i, (r, c) in enumerate(shp))
+        return base.with_(name="wide", wid=140, mats=mats, nesterov=True, weight_decay=0.01, steps=3)
+
+    wl = mk(shapes)
+    rep = []
+    rec = run_gpu(wl, 3, list(range(len(shapes))))
+    check_against_oracle(wl, rec, TOL_O_BF16, report=rep)
+    print("wide tiles worst O rel err", max(e for (_, _, _, e) in rep))
+    rec128 = run_gpu(mk(shapes + [(1152, 8000)]), 3, list(range(len(shapes))))
+    for i in range(len(shapes)):
+        for s, (a, b) in enumerate(zip(rec[i], rec128[i])):
+            for what in ("w_new", "m_new", "o"):
+                assert np.array_equal(getattr(a, what), getattr(b, what)), f"matrix {i} step {s + 1}: {what} differs"
+

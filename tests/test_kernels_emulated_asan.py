@@ -68,16 +68,43 @@ def emu_binary(tmp_path_factory):
     return _build(tmp_path_factory, "emu", [])
 
 
-def _run(exe, case):
+# The 256-wide AXPY kernel, which the library gives only to matrices of at
+# least 2048 on both sides, here for smaller ones, so that full and ragged wide
+# tiles (and the first, middle and last iterations) run in a few seconds.
+WIDE_CASES = [
+    ("256x512,512x256,768x768,500x700,700x500,1x17,300x100", 3, 0, 0),
+    ("256x512,512x256,500x700", 1, 0, 0),
+    ("512x256,700x500,100x300", 2, 0, 0, 5, 1),
+    ("256x512,500x700,300x100", 2, 0, 0, 0, 0, 0, 1),
+    ("512x256,500x700", 2, 0, 0, 0, 0, 0, 0, 1),
+    ("256x512,700x500", 2, 0, 0, 3, 1, 1e15),
+]
+
+
+@pytest.fixture(scope="module")
+def emu_wide_binary(tmp_path_factory):
+    return _build(tmp_path_factory, "emu_wide", ["-DMUON_WIDE_MIN=256"])
+
+
+def _run(exe, case, expect_kernel=None):
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0")
+    if expect_kernel:
+        env["EMU_VERBOSE"] = "1"
     r = subprocess.run([exe, *[str(v) for v in case]], capture_output=True, text=True, env=env, timeout=900)
     assert "AddressSanitizer" not in r.stderr, r.stderr[-3000:]
     assert "runtime error" not in r.stderr, r.stderr[-3000:]
     assert r.returncode == 0, (r.stdout, r.stderr[-2000:])
     assert "step 0" in r.stdout and "adamw 0" in r.stdout
+    if expect_kernel:
+        assert f"launch ({expect_kernel}" in r.stderr or f"launch {expect_kernel}" in r.stderr, r.stderr[-2000:]
 
 
 @pytest.mark.parametrize("case", CASES)
 def test_kernels_stay_in_bounds(emu_binary, case):
     _run(emu_binary, case)
+
+
+@pytest.mark.parametrize("case", WIDE_CASES)
+def test_wide_axpy_stays_in_bounds(emu_wide_binary, case):
+    _run(emu_wide_binary, case, expect_kernel="ns_axpy_wide")
 
