@@ -71,15 +71,14 @@ constexpr int kItemRowsAxpyWhole = 8;
 constexpr int kItemRowsAxpy = 4;
 
 // Tile lists per phase, one per kernel: [0] bf16 iterations on 128-wide
-// tiles, [1] float32 iterations, [2] the bf16 AXPY of large matrices on
-// 256-wide tiles (GRAM and POLY lists [2] stay empty).  A matrix may take the
-// wide AXPY when its padded shape is a multiple of 256 and both sides are at
-// least kWideMinDim (smaller ones have too few wide tiles to fill the CUs:
-// 768-wide matrices measured 3 % slower on them, 1024 x 4096 ones 7 % faster).
-// The wide list is used only when such matrices hold at least half of the
-// AXPY's flops: a phase split over two launches waits for the first one's
-// tail (the MoE stack's four 2048 x 2048 matrices beside 128 experts of
-// 2048 x 1408 measured 4 % slower split).
+// tiles, [1] float32 iterations, [2] bf16 iterations of large matrices on
+// 256-wide tiles.  A matrix may take wide tiles when its padded shape is a
+// multiple of 256 and both sides are at least kWideMinDim (smaller ones have
+// too few wide tiles to fill the CUs: 768-wide matrices measured 3 % slower
+// on them, 1024 x 4096 ones 7 % faster).  A phase uses its wide list only
+// when such matrices hold at least half of its flops: a phase split over two
+// launches waits for the first one's tail (the MoE stack's four 2048 x 2048
+// matrices beside 128 experts of 2048 x 1408 measured 4 % slower split).
 constexpr int kListKinds = 3;
 #ifndef MUON_WIDE_MIN
 #define MUON_WIDE_MIN 1024
@@ -470,30 +469,38 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
         geom[i] = d;
     }
     // Newton-Schulz tile edge: 128 x 128 for every phase and both modes, and
-    // 256 x 256 for the bf16 AXPY of large matrices (kListKinds).  Two 128-wide
+    // 256 x 256 for the bf16 iterations of large matrices (kListKinds).  Two 128-wide
     // workgroups share a CU, so one tile's epilogue overlaps another's main
     // loop; AXPY tiles of this size also keep their quadrant of X from the
     // operand stream.  256-wide tiles of four 128 x 128 waves (one per SIMD)
-    // measured no faster on any workload; the wide AXPY's eight 128 x 64 waves
-    // (two per SIMD) are 7-10 % faster on large matrices.
+    // measured no faster on any workload; wide tiles of eight 128 x 64 waves
+    // (two per SIMD) are faster on large matrices.
     static_assert(kTileBf16 == kTileF32, "one tile edge for both modes");
     auto tile_of = [](int lk) { return lk == 2 ? kTileWide : kTileBf16; };
+    // (every wide-eligible matrix has m >= 1024, so mp = Rp or Cp is a multiple of 256 too)
     auto wide_ok = [&](const MatDesc& d) {
         return !d.f32 && d.Rp % kTileWide == 0 && d.Cp % kTileWide == 0 && std::min(d.R, d.C) >= kWideMinDim;
     };
-    double axpy_flops = 0.0, wide_flops = 0.0;
-    for (int i = 0; i < n; ++i) {
-        if (geom[i].f32) continue;
-        const double f = double(geom[i].R) * geom[i].C * geom[i].m;
-        axpy_flops += f;
-        if (wide_ok(geom[i])) wide_flops += f;
+    // Per phase kind: GRAM, POLY, AXPY.  POLY stays on 128-wide tiles, which
+    // keep A's quadrant from the operand stream for the b A term (wide POLY
+    // measured 1 % faster on the large share, 3 % slower on the 350M-style set).
+    bool use_wide[3] = {};
+    for (int kind : {PH_GRAM, PH_AXPY}) {
+        double all = 0.0, wide = 0.0;
+        for (int i = 0; i < n; ++i) {
+            const MatDesc& d = geom[i];
+            if (d.f32) continue;
+            const double f = double(d.m) * d.m * d.n;   // GRAM and AXPY flops up to a common factor
+            all += f;
+            if (wide_ok(d)) wide += f;
+        }
+        use_wide[kind] = wide > 0.0 && wide >= 0.5 * all;
     }
-    const bool use_wide = wide_flops >= 0.5 * axpy_flops && wide_flops > 0.0;
     // list of entry i in a phase (see kListKinds)
     auto list_kind = [&](int kind, int i) {
         const MatDesc& d = geom[i];
         if (d.f32) return 1;
-        return kind == PH_AXPY && use_wide && wide_ok(d) ? 2 : 0;
+        return use_wide[kind] && wide_ok(d) ? 2 : 0;
     };
     // Tile lists, one per phase and per iteration precision (bf16 and float32
     // entries run different kernels).  Workgroup b runs on XCD b % 8, and each

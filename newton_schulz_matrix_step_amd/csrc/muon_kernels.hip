@@ -1526,7 +1526,7 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 }
 
 // ---------------------------------------------------------------------------
-// Wide AXPY for large matrices: 256 x 256 output tiles, one workgroup of 8
+// Wide tiles for large matrices: 256 x 256 output tiles, one workgroup of 8
 // waves per CU (two per SIMD), each wave a 128 x 64 block (8 x 4 MFMA tiles)
 // instead of 64 x 64.  Per flop it reads a quarter fewer fragment bytes from
 // LDS and streams half the operand bytes from L2 into LDS (the 128-wide
@@ -1534,9 +1534,12 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 // traffic per CU at the MFMA rate, more than the LDS delivers).  k blocks of
 // 64 through two 64 KB LDS stages.  Every output element sums k in the same
 // order as in the 128-wide kernel, so the two give bitwise equal results.
-// The epilogue runs the 128-wide kernel's per-quadrant epilogue on the wave's
-// two 64 x 64 halves, reading the bf16 X from memory (no operand-stream
-// capture: its registers do not fit beside the 128 accumulators).
+// The epilogues are the 128-wide kernel's, run on the wave's two 64 x 64
+// halves, reading from memory what that kernel keeps from the operand stream
+// (AXPY: the bf16 X; POLY: A), whose registers do not fit beside the 128
+// accumulators.  GRAM and POLY take the upper triangle in 256-wide tiles;
+// in a diagonal tile the waves whose block lies wholly below the diagonal
+// skip their MFMAs and epilogue.
 //
 // WideCfg<TM, TN, BK, NST>: TM x TN tile, (TM / 128) x (TN / 64) waves, LDS
 // stages of BK k (a ring of NST).  Measured alternative: 256 x 128 tiles of
@@ -1591,9 +1594,11 @@ __device__ __forceinline__ void issue_wide_load(char* __restrict__ st, const Ope
     else issue_operand_wide<C::TN, C::BK, C::NW, BKC>(st + C::OPA, op.b, op.ldb, row_b0, k0, wave, lane, q - C::LPA);
 }
 
-template <class C, bool AKC, bool BKC>
+// SWAP: feed the MFMA (B fragment, A fragment), the GRAM/POLY accumulator
+// layout; idle: this wave's block needs no output (its loads still go out).
+template <class C, bool AKC, bool BKC, bool SWAP>
 __device__ __forceinline__ void mainloop_wide(char* __restrict__ smem, const Operands& op, int row_a0, int row_b0,
-                                              int wave, int lane, f32x4_t (&acc)[8][4]) {
+                                              int wave, int lane, f32x4_t (&acc)[8][4], bool idle = false) {
     const int wr = (wave / C::WC) * 128, wc = (wave % C::WC) * 64;
     const int nk = (op.K + C::BK - 1) / C::BK;
     // prologue: stages 0 .. NST-2
@@ -1632,24 +1637,26 @@ __device__ __forceinline__ void mainloop_wide(char* __restrict__ smem, const Ope
                 // 1 % faster)
                 if (s == 0 && i < C::LPS && more)
                     issue_wide_load<C, AKC, BKC>(nxt, op, row_a0, row_b0, k_nxt, wave, lane, i);
+                if (idle) continue;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = SWAP ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0)
+                                     : __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
         }
     }
 }
 
 template <int KIND, bool FIRST>
-__global__ __launch_bounds__(WCfg::THREADS, 8 / WCfg::NW) void ns_axpy_wide(const Tile* __restrict__ tiles,
+__global__ __launch_bounds__(WCfg::THREADS, 8 / WCfg::NW) void ns_gemm_wide(const Tile* __restrict__ tiles,
                                                                             const MatDesc* __restrict__ mats,
                                                                             PhaseArgs pa, int n_tiles) {
-    static_assert(KIND == PH_AXPY || KIND == PH_AXPY_LAST, "AXPY phases only");
     using C = WCfg;
     constexpr int TI = 4;   // epilogue quadrant of 4 x 4 MFMA tiles
-    constexpr int EPI_AXPY_BYTES = 16 * (16 * TI + 4) * 4;
+    constexpr bool AXPY = KIND == PH_AXPY || KIND == PH_AXPY_LAST;
+    constexpr int EPI_BYTES = AXPY ? 16 * (16 * TI + 4) * 4 : SymGeom<TI>::T_BYTES;   // per wave
     constexpr int LDS_BYTES = C::NST * C::STB;
-    static_assert(C::NW * EPI_AXPY_BYTES <= LDS_BYTES, "epilogue staging fits the operand stages");
+    static_assert(C::NW * EPI_BYTES <= LDS_BYTES, "epilogue staging fits the operand stages");
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const Tile t = tiles[xcd_tile(blockIdx.x, n_tiles)];
@@ -1659,28 +1666,48 @@ __global__ __launch_bounds__(WCfg::THREADS, 8 / WCfg::NW) void ns_axpy_wide(cons
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row_a0 = t.ti * C::TM, row_b0 = t.tj * C::TN;
+    const int wr = (wave / C::WC) * 128, wc = (wave % C::WC) * 64;
+    const int er0 = row_a0 + wr, ec0 = row_b0 + wc;
 
     f32x4_t acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (op.a_kc && op.b_kc)   // transposed matrix: X^T B
-        mainloop_wide<C, true, true>(smem, op, row_a0, row_b0, wave, lane, acc);
-    else                      // B X
-        mainloop_wide<C, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
-    __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
-
-    constexpr bool LAST = KIND == PH_AXPY_LAST;
-    const AxpyCtx x = axpy_ctx<FIRST>(md, t, pa);
-    const HiCap<TI> cap{};   // not used: the epilogue reads the bf16 X from memory
-    const AxpyRaw<TI> w0[1]{};
-    float* stg = reinterpret_cast<float*>(smem + wave * EPI_AXPY_BYTES);
-    const int er0 = row_a0 + (wave / C::WC) * 128, ec0 = row_b0 + (wave % C::WC) * 64;
-    epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[0]), cap, w0, er0, ec0, lane,
-                                        stg);
-    epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[4]), cap, w0, er0 + 64, ec0,
-                                        lane, stg);
+    if constexpr (AXPY) {
+        if (op.a_kc && op.b_kc)   // transposed matrix: X^T B
+            mainloop_wide<C, true, true, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        else                      // B X
+            mainloop_wide<C, true, false, false>(smem, op, row_a0, row_b0, wave, lane, acc);
+        __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+        constexpr bool LAST = KIND == PH_AXPY_LAST;
+        const AxpyCtx x = axpy_ctx<FIRST>(md, t, pa);
+        const HiCap<TI> cap{};   // not used: the epilogue reads the bf16 X from memory
+        const AxpyRaw<TI> w0[1]{};
+        float* stg = reinterpret_cast<float*>(smem + wave * EPI_BYTES);
+        epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[0]), cap, w0, er0, ec0,
+                                            lane, stg);
+        epi_axpy<TI, FIRST, LAST, false, 0>(x, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[4]), cap, w0, er0 + 64,
+                                            ec0, lane, stg);
+    } else {
+        // GRAM (kc, kc) or, for transposed matrices, (ks, ks); POLY (kc, kc)
+        const bool idle = ec0 + 63 < er0;   // wholly below the diagonal (diagonal tiles only)
+        if (op.a_kc && op.b_kc)
+            mainloop_wide<C, true, true, true>(smem, op, row_a0, row_b0, wave, lane, acc, idle);
+        else
+            mainloop_wide<C, false, false, true>(smem, op, row_a0, row_b0, wave, lane, acc, idle);
+        __syncthreads();   // operand stages are dead: reuse LDS for the epilogue
+        const HiCap<TI> cap{};   // not used: POLY reads A from memory
+        char* tt = smem + wave * EPI_BYTES;
+        // each 64 x 64 half: skipped when wholly below the diagonal; the
+        // epilogue's own element checks handle the halves that cross it
+        if (ec0 + 63 >= er0)
+            epi_sym<KIND, TI, false>(md, t, pa, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[0]), cap, er0, ec0,
+                                     lane, tt);
+        if (ec0 + 63 >= er0 + 64)
+            epi_sym<KIND, TI, false>(md, t, pa, reinterpret_cast<const f32x4_t(&)[TI][TI]>(acc[4]), cap, er0 + 64,
+                                     ec0, lane, tt);
+    }
 }
 
 // FIRST: iteration 1 (X0 read from the momentum pass's copy of u; the master
@@ -1865,16 +1892,18 @@ static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, con
                               mats, a);
         return;
     }
-    if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
-        if (tile == kTileWide) {
-            if (a.iter == 1)
-                hipExtLaunchKernelGGL((ns_axpy_wide<KIND, true>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0, ev1,
+    if (tile == kTileWide) {
+        // only AXPY epilogues differ on the first iteration
+        if constexpr (KIND == PH_AXPY || KIND == PH_AXPY_LAST) {
+            if (a.iter == 1) {
+                hipExtLaunchKernelGGL((ns_gemm_wide<KIND, true>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0, ev1,
                                       0, tiles, mats, a, n_tiles);
-            else
-                hipExtLaunchKernelGGL((ns_axpy_wide<KIND, false>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0,
-                                      ev1, 0, tiles, mats, a, n_tiles);
-            return;
+                return;
+            }
         }
+        hipExtLaunchKernelGGL((ns_gemm_wide<KIND, false>), dim3(n_tiles), dim3(WCfg::THREADS), 0, s, ev0, ev1, 0,
+                              tiles, mats, a, n_tiles);
+        return;
     }
     launch_bf16<KIND, 128>(a.iter == 1, tiles, n_tiles, mats, a, s, ev0, ev1);
 }
@@ -1882,8 +1911,8 @@ static void launch_kind(bool f32c, int tile, const Tile* tiles, int n_tiles, con
 hipError_t launch_ns_phase(int kind, bool f32c, int tile, const Tile* tiles, int n_tiles, const MatDesc* mats,
                            PhaseArgs a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (n_tiles <= 0) return hipSuccess;
-    // 256-wide tiles: bf16 AXPY phases only
-    const bool wide_ok = tile == kTileWide && !f32c && (kind == PH_AXPY || kind == PH_AXPY_LAST);
+    // 256-wide tiles: bf16 iterations only
+    const bool wide_ok = tile == kTileWide && !f32c;
     if (tile != kTileBf16 && !wide_ok) return hipErrorInvalidValue;
     switch (kind) {
         case PH_GRAM: launch_kind<PH_GRAM>(f32c, tile, tiles, n_tiles, mats, a, s, ev0, ev1); break;

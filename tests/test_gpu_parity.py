@@ -743,12 +743,12 @@ def test_small_matrices_run_in_float32():
 
 def test_wide_axpy_tiles():
     """Large matrices (both sides at least 1024, padded shape a multiple of
-    256) run the AXPY on 256-wide tiles when they hold most of the phase's
-    flops.  Their results meet the oracle bars (a ragged 1000 x 2000 matrix
-    among them, every iteration kind over three steps) and equal bitwise those
-    of the 128-wide kernel, which the same matrices take when a larger
-    matrix that cannot use wide tiles (1152 padded rows) dominates the call:
-    both kernels sum every output element's k in the same order."""
+    256) run the GRAM and the AXPY on 256-wide tiles when they hold most of
+    the phase's flops.  Their results meet the oracle bars (a ragged
+    1000 x 2000 matrix among them, every iteration kind over three steps) and
+    equal bitwise those of the 128-wide kernels, which the same matrices take
+    when a larger matrix that cannot use wide tiles (1152 padded rows)
+    dominates the call: both sum every output element's k in the same order."""
     base = workload("gpt2-124m-hidden")
     shapes = [(1024, 2048), (2048, 1024), (1000, 2000), (1024, 1024), (300, 100)]
 

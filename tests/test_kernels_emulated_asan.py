@@ -68,9 +68,9 @@ def emu_binary(tmp_path_factory):
     return _build(tmp_path_factory, "emu", [])
 
 
-# The 256-wide AXPY kernel, which the library gives only to matrices of at
-# least 2048 on both sides, here for smaller ones, so that full and ragged wide
-# tiles (and the first, middle and last iterations) run in a few seconds.
+# The 256-wide kernels, which the library gives only to matrices of at least
+# 1024 on both sides, here for smaller ones, so that full, diagonal and ragged
+# wide tiles (and the first, middle and last iterations) run in a few seconds.
 WIDE_CASES = [
     ("256x512,512x256,768x768,500x700,700x500,1x17,300x100", 3, 0, 0),
     ("256x512,512x256,500x700", 1, 0, 0),
@@ -106,5 +106,5 @@ def test_kernels_stay_in_bounds(emu_binary, case):
 
 @pytest.mark.parametrize("case", WIDE_CASES)
 def test_wide_axpy_stays_in_bounds(emu_wide_binary, case):
-    _run(emu_wide_binary, case, expect_kernel="ns_axpy_wide")
+    _run(emu_wide_binary, case, expect_kernel="ns_gemm_wide")
 
