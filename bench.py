@@ -618,7 +618,8 @@ def main():
     t_mfma, t_hbm = flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
     mfma_frac = t_mfma / dom_avg_s
     hbm_frac = t_hbm / dom_avg_s
-    kname = f"ns_gemm_bf16 ({dom})" if wl.compute == "bf16" else f"ns_gemm_kernel ({dom})"
+    # the phase's launches: 128-wide tiles, and 256-wide ones for large matrices
+    kname = f"ns_gemm_bf16 / ns_gemm_wide ({dom})" if wl.compute == "bf16" else f"ns_gemm_kernel ({dom})"
     if t_mfma >= t_hbm:
         roofline = {"kernel": kname, "bound": "mfma", "achieved": round(flops / dom_avg_s / 1e12, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(mfma_frac, 4)}
