@@ -1537,9 +1537,11 @@ __device__ __forceinline__ void epi_sym(const MatDesc& md, const Tile& t, const 
 // The epilogues are the 128-wide kernel's, run on the wave's two 64 x 64
 // halves, reading from memory what that kernel keeps from the operand stream
 // (AXPY: the bf16 X; POLY: A), whose registers do not fit beside the 128
-// accumulators.  GRAM and POLY take the upper triangle in 256-wide tiles;
-// in a diagonal tile the waves whose block lies wholly below the diagonal
-// skip their MFMAs and epilogue.
+// accumulators.  The symmetric phases take the upper triangle in 256-wide
+// tiles; in a diagonal tile the waves whose block lies wholly below the
+// diagonal skip their MFMAs and epilogue.  (The planner gives wide tiles to
+// the GRAM and the AXPY; POLY keeps its 128-wide kernel, which takes A from
+// the operand stream.)
 //
 // WideCfg<TM, TN, BK, NST>: TM x TN tile, (TM / 128) x (TN / 64) waves, LDS
 // stages of BK k (a ring of NST).  Measured alternative: 256 x 128 tiles of

@@ -60,6 +60,22 @@ def test_noalloc_matches_muon_step_on_two_calls():
         nsm.muon_destroy(h_static)
 
 
+def test_noalloc_wide_tiles_on_two_calls():
+    """Large matrices, whose GRAM and AXPY run on 256-wide tiles, through the
+    static scratch: a call of two 1024 x 2048 / 2048 x 1024 matrices, then a
+    smaller one, each bitwise equal to muon_step."""
+    import torch
+    import newton_schulz_matrix_step_amd as nsm
+    hp = nsm.Hparams()
+    h_plain, h_static = nsm.muon_init(0), nsm.muon_init(0)
+    try:
+        _twin_step(nsm, torch, h_plain, h_static, [(1024, 2048), (2048, 1024)], 73, hp)
+        _twin_step(nsm, torch, h_plain, h_static, [(1024, 1024), (300, 100)], 74, hp)
+    finally:
+        nsm.muon_destroy(h_plain)
+        nsm.muon_destroy(h_static)
+
+
 def test_noalloc_refuses_calls_beyond_the_scratch():
     import torch
     import newton_schulz_matrix_step_amd as nsm
