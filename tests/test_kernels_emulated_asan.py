@@ -108,3 +108,16 @@ def test_kernels_stay_in_bounds(emu_binary, case):
 def test_wide_axpy_stays_in_bounds(emu_wide_binary, case):
     _run(emu_wide_binary, case, expect_kernel="ns_gemm_wide")
 
+
+def test_wide_tiles_only_when_they_carry_most_flops(emu_wide_binary):
+    """The planner gives a phase wide tiles only when the matrices that can
+    take them carry at least half of its flops: alone, a 256 x 512 matrix
+    runs its GRAM and AXPY on wide tiles; beside a dominant 300 x 2000 one
+    (padded rows not a multiple of 256) every matrix stays on 128-wide tiles."""
+    _run(emu_wide_binary, ("256x512", 2, 0, 0), expect_kernel="ns_gemm_wide")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", EMU_VERBOSE="1")
+    r = subprocess.run([emu_wide_binary, "256x512,300x2000", "2", "0", "0"], capture_output=True, text=True, env=env,
+                       timeout=900)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "ns_gemm_wide" not in r.stderr and "ns_gemm_bf16" in r.stderr
+
