@@ -64,9 +64,12 @@ constexpr int64_t kMaxEntries = 65536;   // plan entries (matrices or blocks) pe
 constexpr int kUnitElems = MUON_UNIT_ELEMS;  // momentum-pass elements per workgroup (target)
 
 // Tile rows per item of the tile lists (see build_list): GRAM / POLY items of
-// 8 rows; an AXPY output of at most 8 tile rows is one item, taller ones go in
-// items of 4 rows (8 measured slower there).
+// 8 rows (4 rows of 256-wide tiles: 5 % faster than 8 or 16 on the large
+// layer share's GRAM); an AXPY output of at most 8 tile rows is one item,
+// taller ones go in items of 4 rows (8 measured slower there, also for
+// 256-wide tiles).
 constexpr int kItemRowsSym = 8;
+constexpr int kItemRowsWideSym = 4;
 constexpr int kItemRowsAxpyWhole = 8;
 constexpr int kItemRowsAxpy = 4;
 
@@ -531,7 +534,10 @@ muon_status layout_plan(muon_handle* h, const std::vector<MatIn>& mats, bool f32
             tm = sym ? (d.m + T - 1) / T : (d.R + T - 1) / T;
             tn = sym ? tm : (d.C + T - 1) / T;
         };
-        auto item_rows = [&](int tm) { return sym ? kItemRowsSym : (tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy); };
+        auto item_rows = [&](int tm) {
+            if (sym) return lk == 2 ? kItemRowsWideSym : kItemRowsSym;
+            return tm <= kItemRowsAxpyWhole ? tm : kItemRowsAxpy;
+        };
         for (int i = 0; i < n; ++i) {
             if (list_kind(kind, i) != lk) continue;
             int tm, tn;
