@@ -1,14 +1,19 @@
 // Test infrastructure: runs muon_step and muon_adamw_step of the library, built
 // against the CPU stand-in of HIP (tests/emu/hip), on exactly sized host
 // buffers, so AddressSanitizer reports any access outside a caller buffer or
-// the workspace.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT [GRAD [NOALLOC [DEBUG]]]]]]
+// the workspace.  The stand-in runs the momentum pass's element arithmetic for
+// real, so every new momentum element is also checked against beta m + g
+// (position-dependent values, so a wrong index shows) and the padding between
+// rows against its old value.  Usage: emu_driver SHAPES NS_STEPS DTYPE [BLOCK_ROWS [LD_PAD [SHIFT [GRAD [NOALLOC [DEBUG]]]]]]
 //   SHAPES "RxC,RxC,...", DTYPE 0 = bf16, 1 = f32 (also selects fp32 compute),
 //   BLOCK_ROWS > 0 cuts every matrix whose rows it divides into row blocks,
 //   LD_PAD extra elements per row (views into wider buffers), SHIFT elements
 //   by which every buffer starts past its allocation (unaligned bases).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -20,6 +25,10 @@ emu_idx threadIdx, blockIdx;
 dim3 gridDim, blockDim;
 long emu_launches = 0;
 int emu_verbose = 0;
+
+// position-dependent values, exact in bf16 (multiples of 1/16 up to 14/16)
+static float grad_at(long i, long j) { return float((i * 37 + j * 11) % 29 - 14) * 0.0625f; }
+static float mom_at(long q) { return float((q * 13) % 23 - 11) * 0.125f; }
 
 int main(int argc, char** argv) {
     if (argc < 4) return 2;
@@ -57,7 +66,7 @@ int main(int argc, char** argv) {
         void* g = buf(r, ld, c, es);
         for (long i = 0; i < r; ++i)
             for (long j = 0; j < c; ++j) {
-                const float v = float(gval);
+                const float v = gval != 0.0 ? float(gval) : grad_at(i, j);
                 if (es == 4) {
                     static_cast<float*>(g)[i * ld + j] = v;
                 } else {
@@ -68,6 +77,7 @@ int main(int argc, char** argv) {
             }
         m.grad = g;
         m.momentum = static_cast<float*>(buf(r, ld, c, 4));
+        for (long q = 0; q < (r - 1) * ld + c; ++q) m.momentum[q] = mom_at(q);
         m.update_out = static_cast<float*>(buf(r, ld, c, 4));
         m.rows = r;
         m.cols = c;
@@ -89,6 +99,33 @@ int main(int argc, char** argv) {
         st = muon_step(h, mats.data(), static_cast<int>(mats.size()), &hp, nullptr);
     }
     std::printf("step %d (%s) launches %ld\n", st, muon_last_error(h), emu_launches);
+    // momentum: matrix k went through `calls` steps (the no-allocation run
+    // repeats the first matrix alone); padding keeps its value
+    long bad = 0;
+    for (size_t k = 0; k < mats.size() && st == MUON_OK; ++k) {
+        const muon_matrix& m = mats[k];
+        const int calls = noalloc && k == 0 ? 2 : 1;
+        for (long q = 0; q < (m.rows - 1) * m.ld_mom + m.cols; ++q) {
+            const long i = q / m.ld_mom, j = q % m.ld_mom;
+            float want = mom_at(q);
+            if (j < m.cols) {
+                float gv;
+                if (gval != 0.0) gv = float(gval);
+                else gv = grad_at(i, j);
+                if (es == 2) {   // the stored bf16 gradient
+                    uint32_t u;
+                    std::memcpy(&u, &gv, 4);
+                    u &= 0xFFFF0000u;
+                    std::memcpy(&gv, &u, 4);
+                }
+                for (int t = 0; t < calls; ++t) want = std::fmaf(hp.beta, want, gv);
+            }
+            if (m.momentum[q] != want && bad++ < 5)
+                std::printf("momentum of matrix %zu at (%ld, %ld): %g, want %g\n", k, i, j, m.momentum[q], want);
+        }
+    }
+    std::printf("momentum mismatches %ld\n", bad);
+    if (bad) st = -1;
     // AdamW over ragged sizes: vector path, ragged tail and scalar path
     const long sizes[5] = {1, 4095, 4096, 4097, 10001};
     std::vector<muon_adamw_tensor> ts;
